@@ -1,0 +1,15 @@
+"""Plain, slow CPU oracle (float64 numpy) for the Hybrid Linear-Softmax
+Attention group.  Test infrastructure only: the test suite, the smoke check and
+the bench's CPU-baseline leg use it; the library path never does."""
+from .hybrid_ref import (  # noqa: F401
+    EPS,
+    SCHEDULE,
+    phi,
+    sigmoid,
+    kv_state,
+    linear_attention,
+    linear_attention_bruteforce,
+    softmax_attention,
+    layer,
+    group,
+)

@@ -1,0 +1,124 @@
+"""Seeded synthetic Q, K, V, G for one attention layer or a stacked 4-layer group.
+
+Recipe (same for every workload):
+  * one independent random stream per (layer, tensor) -- or per (layer, tensor,
+    b, h) slab for the on-device generator -- derived from the workload seed with
+    numpy's SeedSequence spawn keys, tensor ids Q=0, K=1, V=2, G=3, heavy-row
+    set=4;
+  * standard normal draws in float32, scaled to the workload's distribution
+    (Q, K, V ~ N(0,1) or N(0,1)/sqrt(d); G ~ N(g_mean, 1));
+  * heavy-tailed workloads scale round(heavy_frac * N) token rows of K and V by
+    heavy_scale; the rows are drawn without replacement, shared by K and V, by
+    every batch item and head of one layer;
+  * rounding to the storage dtype with round-to-nearest-even (torch's float32 ->
+    bfloat16 conversion).
+The host generator (numpy PCG64) and the device generator (torch Philox, used
+where host generation of multi-GB tensors would take minutes) draw different
+numbers for the same seed; a check always hands the oracle the exact values the
+GPU saw, copied back from device memory.
+"""
+import math
+
+import numpy as np
+import torch
+
+from .configs import Workload
+
+TENSORS = ("Q", "K", "V", "G")
+_TID = {"Q": 0, "K": 1, "V": 2, "G": 3, "heavy": 4}
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def torch_dtype(w: Workload):
+    return _TORCH_DTYPE[w.dtype]
+
+
+def _std(w: Workload, name: str) -> float:
+    if name == "G":
+        return 1.0
+    return 1.0 if w.qkv_std == "unit" else 1.0 / math.sqrt(w.d)
+
+
+def _mean(w: Workload, name: str) -> float:
+    return w.g_mean if name == "G" else 0.0
+
+
+def _seed_seq(w: Workload, layer: int, name: str, *slab):
+    return np.random.SeedSequence(w.seed, spawn_key=(layer, _TID[name]) + tuple(slab))
+
+
+def heavy_token_positions(w: Workload, layer: int, N: int | None = None) -> np.ndarray:
+    """Sorted token indices whose K and V rows are scaled (empty if none)."""
+    N = w.N if N is None else N
+    n_heavy = int(round(w.heavy_frac * N))
+    if n_heavy == 0:
+        return np.zeros(0, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(_seed_seq(w, layer, "heavy")))
+    return np.sort(rng.choice(N, size=n_heavy, replace=False)).astype(np.int64)
+
+
+def layer_inputs_host(w: Workload, layer: int = 0, *, B=None, H=None, N=None,
+                      device="cpu") -> dict:
+    """Q, K, V, G of one layer drawn on the host, returned as torch tensors of the
+    workload dtype on `device`.  B, H, N override the workload's sizes (tests use
+    smaller shapes with the same distributions)."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    heavy = heavy_token_positions(w, layer, N)
+    out = {}
+    for name in TENSORS:
+        rng = np.random.Generator(np.random.PCG64(_seed_seq(w, layer, name)))
+        x = rng.standard_normal((B, H, N, w.d), dtype=np.float32)
+        x *= np.float32(_std(w, name))
+        if _mean(w, name) != 0.0:
+            x += np.float32(_mean(w, name))
+        if name in ("K", "V") and heavy.size:
+            x[:, :, heavy, :] *= np.float32(w.heavy_scale)
+        out[name] = torch.from_numpy(x).to(torch_dtype(w)).to(device)
+    return out
+
+
+def _torch_seed(w: Workload, layer: int, name: str, *slab) -> int:
+    return int(_seed_seq(w, layer, name, *slab).generate_state(1, np.uint64)[0] >> 1)
+
+
+def layer_inputs_device(w: Workload, layer: int = 0, device="cuda", *, out=None) -> dict:
+    """Q, K, V, G of one layer drawn on the GPU, one (b, h) slab at a time so the
+    float32 staging buffer stays at N*d elements.  `out` may hold preallocated
+    [B, H, N, d] tensors (e.g. views into a stacked group buffer)."""
+    heavy = heavy_token_positions(w, layer)
+    heavy_t = torch.from_numpy(heavy).to(device) if heavy.size else None
+    res = {}
+    gen = torch.Generator(device=device)
+    for name in TENSORS:
+        t = out[name] if out is not None else torch.empty(
+            (w.B, w.H, w.N, w.d), dtype=torch_dtype(w), device=device)
+        for b in range(w.B):
+            for h in range(w.H):
+                gen.manual_seed(_torch_seed(w, layer, name, b, h))
+                x = torch.randn((w.N, w.d), generator=gen, device=device, dtype=torch.float32)
+                x.mul_(_std(w, name))
+                if _mean(w, name) != 0.0:
+                    x.add_(_mean(w, name))
+                if name in ("K", "V") and heavy_t is not None:
+                    x.index_mul_(0, heavy_t, torch.full((heavy_t.numel(), 1), w.heavy_scale,
+                                                        device=device).expand(-1, w.d).contiguous())
+                t[b, h].copy_(x)
+                del x
+        res[name] = t
+    return res
+
+
+def group_inputs_device(w: Workload, device="cuda", layers: int = 4) -> dict:
+    """Stacked [layers, B, H, N, d] Q, K, V, G for a group, drawn on the GPU."""
+    stacked = {n: torch.empty((layers, w.B, w.H, w.N, w.d), dtype=torch_dtype(w), device=device)
+               for n in TENSORS}
+    for layer in range(layers):
+        layer_inputs_device(w, layer, device, out={n: stacked[n][layer] for n in TENSORS})
+    return stacked
+
+
+def to_f64(t) -> np.ndarray:
+    """Exact widening of a float32/bfloat16 tensor to a float64 numpy array."""
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
