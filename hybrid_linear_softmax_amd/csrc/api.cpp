@@ -1,0 +1,246 @@
+// C ABI of libhybrid_attn.so: argument validation (host only, before any HIP
+// call) and the launch sequence of each entry point.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/hybrid_attn.h"
+#include "ha_launch.h"
+
+namespace {
+
+struct Problem {
+  int64_t B, H, N, d, BH;
+  bool bf16;
+  size_t tensor_bytes;  // bytes of one [B, H, N, d] tensor
+};
+
+int check_shape(int B, int H, int64_t N, int d, int dtype, Problem* p) {
+  if (dtype != HA_BF16 && dtype != HA_F32) return HA_EUNSUPPORTED;
+  if (d != 64 && d != 128) return HA_EUNSUPPORTED;
+  if (B < 0 || H < 0 || N < 0) return HA_EINVAL;
+  if (N > HA_MAX_N) return HA_EINVAL;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (BH > HA_MAX_BH) return HA_EINVAL;
+  p->B = B;
+  p->H = H;
+  p->N = N;
+  p->d = d;
+  p->BH = BH;
+  p->bf16 = dtype == HA_BF16;
+  p->tensor_bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * static_cast<size_t>(d) *
+                    (p->bf16 ? 2u : 4u);
+  return HA_OK;
+}
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Null, alignment and aliasing checks of n_in inputs and one output.
+int check_buffers(const void* const* in, int n_in, size_t in_bytes, const void* out,
+                  size_t out_bytes) {
+  for (int i = 0; i < n_in; ++i)
+    if (in[i] == nullptr) return HA_EINVAL;
+  if (out == nullptr) return HA_EINVAL;
+  for (int i = 0; i < n_in; ++i)
+    if (misaligned(in[i])) return HA_EALIGN;
+  if (misaligned(out)) return HA_EALIGN;
+  for (int i = 0; i < n_in; ++i)
+    if (overlaps(in[i], in_bytes, out, out_bytes)) return HA_EINVAL;
+  return HA_OK;
+}
+
+int check_workspace(const Problem& p, const void* ws, size_t ws_bytes) {
+  const size_t need = ha::linear_ws(p.BH, p.N, static_cast<int>(p.d), p.bf16).total;
+  if (ws == nullptr || ws_bytes < need) return HA_EWORKSPACE;
+  if (misaligned(ws)) return HA_EALIGN;
+  return HA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HA_OK : HA_EHIP; }
+
+// One linear layer on validated arguments.
+int run_linear(const Problem& p, const void* Q, const void* K, const void* V, const void* G,
+               void* O, void* ws, hipStream_t s) {
+  const int d = static_cast<int>(p.d);
+  const ha::LinearWs L = ha::linear_ws(p.BH, p.N, d, p.bf16);
+  char* w = static_cast<char*>(ws);
+  float* part = reinterpret_cast<float*>(w + L.part);
+  float* S = reinterpret_cast<float*>(w + L.S);
+  float* z = reinterpret_cast<float*>(w + L.z);
+  uint16_t* hi = reinterpret_cast<uint16_t*>(w + L.St_hi);
+  uint16_t* lo = reinterpret_cast<uint16_t*>(w + L.St_lo);
+  const ha::KvSplit sp = ha::kv_split(p.BH, p.N);
+  hipError_t e = ha::launch_kv_partials(p.bf16, d, K, V, part, p.BH, p.N, sp, s);
+  if (e != hipSuccess) return HA_EHIP;
+  e = ha::launch_kv_reduce(p.bf16, d, part, S, z, hi, lo, p.BH, sp.chunks, s);
+  if (e != hipSuccess) return HA_EHIP;
+  e = ha::launch_apply(p.bf16, d, Q, G, O, S, z, hi, lo, p.BH, p.N, HA_LINEAR_EPS, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+namespace ha {
+
+LinearWs linear_ws(int64_t BH, int64_t N, int d, bool bf16) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const KvSplit sp = kv_split(BH, N);
+  const size_t dd = static_cast<size_t>(d) * d;
+  LinearWs L{};
+  size_t off = 0;
+  L.part = off;
+  off += up(static_cast<size_t>(BH) * sp.chunks * (dd + d) * sizeof(float));
+  L.S = off;
+  off += up(static_cast<size_t>(BH) * dd * sizeof(float));
+  L.z = off;
+  off += up(static_cast<size_t>(BH) * d * sizeof(float));
+  L.St_hi = off;
+  if (bf16) off += up(static_cast<size_t>(BH) * dd * sizeof(uint16_t));
+  L.St_lo = off;
+  if (bf16) off += up(static_cast<size_t>(BH) * dd * sizeof(uint16_t));
+  L.total = off;
+  return L;
+}
+
+}  // namespace ha
+
+extern "C" {
+
+HA_API const char* hybrid_attn_strerror(int status) {
+  switch (status) {
+    case HA_OK: return "success";
+    case HA_EINVAL: return "invalid argument (size, null pointer or output overlapping an input)";
+    case HA_EUNSUPPORTED: return "unsupported head dimension or dtype (d must be 64 or 128; dtype bf16 or f32)";
+    case HA_EALIGN: return "pointer not 16-byte aligned";
+    case HA_EWORKSPACE: return "workspace missing or smaller than hybrid_attn_workspace_bytes()";
+    case HA_EHIP: return "HIP kernel launch or event record failed";
+    default: return "unknown status";
+  }
+}
+
+HA_API size_t hybrid_attn_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype) {
+  Problem p;
+  if (check_shape(B, H, N, d, dtype, &p) != HA_OK || p.BH == 0) return 0;
+  return ha::linear_ws(p.BH, p.N, d, p.bf16).total;
+}
+
+HA_API int hybrid_attn_kv_state(const void* K, const void* V, float* S, float* z, int B, int H,
+                                int64_t N, int d, ha_dtype dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0) return HA_OK;
+  const size_t s_bytes = static_cast<size_t>(p.BH) * d * d * sizeof(float);
+  const size_t z_bytes = static_cast<size_t>(p.BH) * d * sizeof(float);
+  if (S == nullptr || z == nullptr) return HA_EINVAL;
+  if (p.N > 0) {
+    const void* in[2] = {K, V};
+    st = check_buffers(in, 2, p.tensor_bytes, S, s_bytes);
+    if (st != HA_OK) return st;
+    st = check_buffers(in, 2, p.tensor_bytes, z, z_bytes);
+    if (st != HA_OK) return st;
+  } else if (misaligned(S) || misaligned(z)) {
+    return HA_EALIGN;
+  }
+  if (overlaps(S, s_bytes, z, z_bytes)) return HA_EINVAL;
+  st = check_workspace(p, workspace, workspace_bytes);
+  if (st != HA_OK) return st;
+
+  const ha::LinearWs L = ha::linear_ws(p.BH, p.N, d, p.bf16);
+  char* w = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(w + L.part);
+  const ha::KvSplit sp = ha::kv_split(p.BH, p.N);
+  hipError_t e = ha::launch_kv_partials(p.bf16, d, K, V, part, p.BH, p.N, sp, stream);
+  if (e != hipSuccess) return HA_EHIP;
+  // the exported state is float32 only: no bf16 split needed here
+  e = ha::launch_kv_reduce(false, d, part, S, z, nullptr, nullptr, p.BH, sp.chunks, stream);
+  return hip_status(e);
+}
+
+HA_API int hybrid_attn_linear(const void* Q, const void* K, const void* V, const void* G, void* O,
+                              int B, int H, int64_t N, int d, ha_dtype dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const void* in[4] = {Q, K, V, G};
+  st = check_buffers(in, 4, p.tensor_bytes, O, p.tensor_bytes);
+  if (st != HA_OK) return st;
+  st = check_workspace(p, workspace, workspace_bytes);
+  if (st != HA_OK) return st;
+  return run_linear(p, Q, K, V, G, O, workspace, stream);
+}
+
+HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, const void* G, void* O,
+                               int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const void* in[4] = {Q, K, V, G};
+  st = check_buffers(in, 4, p.tensor_bytes, O, p.tensor_bytes);
+  if (st != HA_OK) return st;
+  return hip_status(ha::launch_anchor(p.bf16, d, Q, K, V, G, O, p.BH, p.N, stream));
+}
+
+HA_API int hybrid_attn_group_timed(const void* Q4, const void* K4, const void* V4, const void* G4,
+                                   void* O4, int B, int H, int64_t N, int d, ha_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t const events[5]) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (events != nullptr)
+    for (int i = 0; i < 5; ++i)
+      if (events[i] == nullptr) return HA_EINVAL;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const size_t group_bytes = 4 * p.tensor_bytes;
+  const void* in[4] = {Q4, K4, V4, G4};
+  st = check_buffers(in, 4, group_bytes, O4, group_bytes);
+  if (st != HA_OK) return st;
+  st = check_workspace(p, workspace, workspace_bytes);
+  if (st != HA_OK) return st;
+
+  int kinds[4];
+  hybrid_attn_group_schedule(kinds);
+  if (events != nullptr && hipEventRecord(events[0], stream) != hipSuccess) return HA_EHIP;
+  for (int l = 0; l < 4; ++l) {
+    const size_t off = static_cast<size_t>(l) * p.tensor_bytes;
+    const char* q = static_cast<const char*>(Q4) + off;
+    const char* k = static_cast<const char*>(K4) + off;
+    const char* v = static_cast<const char*>(V4) + off;
+    const char* g = static_cast<const char*>(G4) + off;
+    char* o = static_cast<char*>(O4) + off;
+    if (kinds[l] == 0)
+      st = run_linear(p, q, k, v, g, o, workspace, stream);
+    else
+      st = hip_status(ha::launch_anchor(p.bf16, d, q, k, v, g, o, p.BH, p.N, stream));
+    if (st != HA_OK) return st;
+    if (events != nullptr && hipEventRecord(events[l + 1], stream) != hipSuccess) return HA_EHIP;
+  }
+  return HA_OK;
+}
+
+HA_API int hybrid_attn_group(const void* Q4, const void* K4, const void* V4, const void* G4, void* O4,
+                             int B, int H, int64_t N, int d, ha_dtype dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return hybrid_attn_group_timed(Q4, K4, V4, G4, O4, B, H, N, d, dtype, workspace, workspace_bytes,
+                                 stream, nullptr);
+}
+
+HA_API int hybrid_attn_group_schedule(int kinds[4]) {
+  if (kinds == nullptr) return HA_EINVAL;
+  static const int schedule[4] = {0, 0, 0, 1};
+  memcpy(kinds, schedule, sizeof(schedule));
+  return HA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Host-side launchers of the gfx950 kernels (internal to libhybrid_attn.so).
+// Each returns the hipError_t of its launch(es); shapes are validated by the
+// C-ABI layer before any of these is called.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace ha {
+
+// Token split of the linear-state reduction: a pure function of (BH, N), never
+// of the device, so the reduction order (and the result) is reproducible.
+struct KvSplit {
+  int64_t chunk_len;  // tokens per chunk, a multiple of 64
+  int64_t chunks;     // ceil(N / chunk_len), 0 when N == 0
+};
+KvSplit kv_split(int64_t BH, int64_t N);
+
+// Workspace layout of the linear layer (byte offsets from the workspace base).
+struct LinearWs {
+  size_t part;    // float [BH][chunks][d*d + d]  per-chunk partial S, z
+  size_t S;       // float [BH][d][d]             reduced S (row = key feature)
+  size_t z;       // float [BH][d]                reduced z
+  size_t St_hi;   // bf16  [BH][d][d]             S^T split hi (bf16 path only)
+  size_t St_lo;   // bf16  [BH][d][d]             S^T - hi, rounded (bf16 path only)
+  size_t total;
+};
+LinearWs linear_ws(int64_t BH, int64_t N, int d, bool bf16);
+
+// R1 pass 1: per (bh, chunk) partial state into part.
+hipError_t launch_kv_partials(bool bf16, int d, const void* K, const void* V, float* part,
+                              int64_t BH, int64_t N, KvSplit split, hipStream_t s);
+// R1 pass 2: fixed-order sum over chunks into S, z (and the bf16 hi/lo S^T).
+hipError_t launch_kv_reduce(bool bf16, int d, const float* part, float* S, float* z,
+                            uint16_t* St_hi, uint16_t* St_lo, int64_t BH, int64_t chunks,
+                            hipStream_t s);
+// R2: fused apply phi(Q) S / (phi(Q) z + eps), sigmoid gate, store.
+hipError_t launch_apply(bool bf16, int d, const void* Q, const void* G, void* O, const float* S,
+                        const float* z, const uint16_t* St_hi, const uint16_t* St_lo, int64_t BH,
+                        int64_t N, float eps, hipStream_t s);
+// R3: gated softmax anchor (flash-style, online softmax).
+hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const void* V,
+                         const void* G, void* O, int64_t BH, int64_t N, hipStream_t s);
+
+}  // namespace ha

@@ -1,0 +1,314 @@
+// Linear-attention state reduction (the O(N) half of the gated linear layer:
+// SANA-Video 2.0 summary page, section 03; review page, section 1):
+//   S = sum_j phi(k_j) v_j^T  (d x d),   z = sum_j phi(k_j)  (d),   phi = ReLU,
+// for every (batch, head).  Pass 1 splits the N tokens of a head into fixed
+// chunks and writes one partial (S_c, z_c) per chunk; pass 2 adds the partials
+// in chunk order.  No atomics: the result is bitwise reproducible.
+//
+// bf16 pass 1 is an MFMA contraction over tokens: phi(K_c)^T V_c.  Both
+// operands need "8 consecutive tokens of one feature" per lane, while K and V
+// are stored token-major, so each 64-token tile is transposed on its way into
+// LDS (4 tokens x 8 features per thread, in registers) and the MFMA operands
+// are then plain 16-byte LDS reads.  The kernel is HBM-bound (64 flop/byte at
+// d = 128), the MFMA work keeps the VALU free for the transpose.
+#include "ha_device.h"
+#include "ha_launch.h"
+
+namespace ha {
+
+namespace {
+
+constexpr int kTile = 64;  // tokens per pass-1 tile
+
+// ---------------------------------------------------------------- bf16 pass 1
+template <int D>
+__global__ __launch_bounds__(256) void kv_partials_bf16(const bf16_t* __restrict__ K,
+                                                        const bf16_t* __restrict__ V,
+                                                        float* __restrict__ part, int64_t N,
+                                                        int64_t chunk_len, int64_t chunks) {
+  constexpr int P = kTile + 8;            // LDS pitch (elements) of a transposed row
+  constexpr int FG = D / 8;               // 16-byte feature groups per token row
+  constexpr int SUB = (kTile / 4) * FG;   // 4-token x 8-feature sub-tiles per tensor
+  constexpr int PER = 2 * SUB / 256;      // sub-tiles per thread (K and V together)
+  constexpr int RB = D / 64;              // 32x32 output blocks per wave, per dim
+  __shared__ __attribute__((aligned(16))) bf16_t sK[D * P];  // phi(K)^T tile [feature][token]
+  __shared__ __attribute__((aligned(16))) bf16_t sV[D * P];  // V^T tile      [feature][token]
+  __shared__ float sZ[kTile / 4][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t bh = blockIdx.x / chunks;
+  const int64_t c = blockIdx.x % chunks;
+  const int64_t t_begin = c * chunk_len;
+  const int64_t t_end = min(N, t_begin + chunk_len);
+  const bf16_t* Kh = K + bh * N * D;
+  const bf16_t* Vh = V + bh * N * D;
+
+  // sub-tile u of this thread: tensor u / SUB, feature group, 4-token group
+  int sub_fg[PER], sub_m[PER];
+  bool sub_k[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int u = tid + 256 * i;
+    sub_k[i] = u < SUB;
+    const int w = u % SUB;
+    sub_fg[i] = w % FG;
+    sub_m[i] = w / FG;
+  }
+
+  uint4 regs[PER][4];
+  auto load_tile = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bf16_t* src = sub_k[i] ? Kh : Vh;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tok = t0 + 4 * sub_m[i] + r;
+        regs[i][r] = tok < t_end
+                         ? *reinterpret_cast<const uint4*>(src + tok * D + 8 * sub_fg[i])
+                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  float zacc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) zacc[k] = 0.f;
+
+  f32x16 acc[RB][RB];
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // wave's output block: rows (key features) ra.., cols (value features) cj..
+  const int ra = (wave >> 1) * 32 * RB;
+  const int cj = (wave & 1) * 32 * RB;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  load_tile(t_begin);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTile) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      uint4 w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = sub_k[i] ? relu8(regs[i][r]) : regs[i][r];
+      if (sub_k[i]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          zacc[0] += bf_lo(w[r].x); zacc[1] += bf_hi(w[r].x);
+          zacc[2] += bf_lo(w[r].y); zacc[3] += bf_hi(w[r].y);
+          zacc[4] += bf_lo(w[r].z); zacc[5] += bf_hi(w[r].z);
+          zacc[6] += bf_lo(w[r].w); zacc[7] += bf_hi(w[r].w);
+        }
+      }
+      uint2 tr[8];
+      transpose4x8(w, tr);
+      bf16_t* dst = sub_k[i] ? sK : sV;
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+        *reinterpret_cast<uint2*>(dst + (8 * sub_fg[i] + f) * P + 4 * sub_m[i]) = tr[f];
+    }
+    __syncthreads();
+    if (t0 + kTile < t_end) load_tile(t0 + kTile);
+#pragma unroll
+    for (int s = 0; s < kTile / 16; ++s) {
+      bf16x8 af[RB], bfr[RB];
+#pragma unroll
+      for (int a = 0; a < RB; ++a)
+        af[a] = *reinterpret_cast<const bf16x8*>(sK + (ra + 32 * a + l32) * P + 16 * s + 8 * h);
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+        bfr[b] = *reinterpret_cast<const bf16x8*>(sV + (cj + 32 * b + l32) * P + 16 * s + 8 * h);
+#pragma unroll
+      for (int a = 0; a < RB; ++a)
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    }
+  }
+
+  float* out = part + (bh * chunks + c) * (int64_t)(D * D + D);
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = ra + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int col = cj + 32 * b + l32;
+        out[row * D + col] = acc[a][b][r];
+      }
+
+  // z: the thread holding K sub-tile (fg, m) summed 8 features over its tokens;
+  // add the 16 token groups of each feature in a fixed order.
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (sub_k[i])
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sZ[sub_m[i]][8 * sub_fg[i] + k] = zacc[k];
+  __syncthreads();
+  if (tid < D) {
+    float zs = 0.f;
+#pragma unroll
+    for (int m = 0; m < kTile / 4; ++m) zs += sZ[m][tid];
+    out[D * D + tid] = zs;
+  }
+}
+
+// ---------------------------------------------------------------- f32 pass 1
+// Plain VALU contraction: thread (ta, tj) owns S rows ta + 16x, columns tj + 16y.
+template <int D>
+__global__ __launch_bounds__(256) void kv_partials_f32(const float* __restrict__ K,
+                                                       const float* __restrict__ V,
+                                                       float* __restrict__ part, int64_t N,
+                                                       int64_t chunk_len, int64_t chunks) {
+  constexpr int T = 32;
+  constexpr int R = D / 16;
+  __shared__ __attribute__((aligned(16))) float sK[T][D];
+  __shared__ __attribute__((aligned(16))) float sV[T][D];
+  const int tid = threadIdx.x;
+  const int ta = tid >> 4, tj = tid & 15;
+  const int64_t bh = blockIdx.x / chunks;
+  const int64_t c = blockIdx.x % chunks;
+  const int64_t t_begin = c * chunk_len;
+  const int64_t t_end = min(N, t_begin + chunk_len);
+  const float* Kh = K + bh * N * D;
+  const float* Vh = V + bh * N * D;
+
+  float acc[R][R];
+  float zacc[R];
+#pragma unroll
+  for (int x = 0; x < R; ++x) {
+    zacc[x] = 0.f;
+#pragma unroll
+    for (int y = 0; y < R; ++y) acc[x][y] = 0.f;
+  }
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+    __syncthreads();
+    for (int e = tid; e < T * D / 4; e += 256) {
+      const int row = e / (D / 4), col = 4 * (e % (D / 4));
+      const int64_t tok = t0 + row;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (tok < t_end) {
+        kv = *reinterpret_cast<const float4*>(Kh + tok * D + col);
+        vv = *reinterpret_cast<const float4*>(Vh + tok * D + col);
+      }
+      kv.x = fmaxf(kv.x, 0.f); kv.y = fmaxf(kv.y, 0.f);
+      kv.z = fmaxf(kv.z, 0.f); kv.w = fmaxf(kv.w, 0.f);
+      *reinterpret_cast<float4*>(&sK[row][col]) = kv;
+      *reinterpret_cast<float4*>(&sV[row][col]) = vv;
+    }
+    __syncthreads();
+    for (int n = 0; n < T; ++n) {
+      float kr[R], vr[R];
+#pragma unroll
+      for (int x = 0; x < R; ++x) kr[x] = sK[n][ta + 16 * x];
+#pragma unroll
+      for (int y = 0; y < R; ++y) vr[y] = sV[n][tj + 16 * y];
+#pragma unroll
+      for (int x = 0; x < R; ++x) {
+        zacc[x] += kr[x];
+#pragma unroll
+        for (int y = 0; y < R; ++y) acc[x][y] = fmaf(kr[x], vr[y], acc[x][y]);
+      }
+    }
+  }
+  float* out = part + (bh * chunks + c) * (int64_t)(D * D + D);
+#pragma unroll
+  for (int x = 0; x < R; ++x)
+#pragma unroll
+    for (int y = 0; y < R; ++y) out[(ta + 16 * x) * D + tj + 16 * y] = acc[x][y];
+  if (tj == 0)
+#pragma unroll
+    for (int x = 0; x < R; ++x) out[D * D + ta + 16 * x] = zacc[x];
+}
+
+// ---------------------------------------------------------------- pass 2
+// Element e of (S, z) of one head: sum over chunks in order.  The bf16 path also
+// stores S^T split into bf16 hi + lo (hi = rne(s), lo = rne(s - hi)), the layout
+// the apply kernel's MFMA B operand reads.
+template <int D>
+__global__ __launch_bounds__(256) void kv_reduce(const float* __restrict__ part,
+                                                 float* __restrict__ S, float* __restrict__ z,
+                                                 bf16_t* __restrict__ St_hi,
+                                                 bf16_t* __restrict__ St_lo, int64_t chunks,
+                                                 int blocks_per_head) {
+  constexpr int E = D * D + D;
+  const int64_t bh = blockIdx.x / blocks_per_head;
+  const int e = (blockIdx.x % blocks_per_head) * 256 + threadIdx.x;
+  if (e >= E) return;
+  const float* p = part + bh * chunks * (int64_t)E + e;
+  float s = 0.f;
+  for (int64_t c = 0; c < chunks; ++c) s += p[c * E];
+  if (e < D * D) {
+    S[bh * D * D + e] = s;
+    if (St_hi != nullptr) {
+      const int a = e / D, j = e % D;
+      const bf16_t hi = to_bf16(s);
+      const float hif = __uint_as_float(static_cast<uint32_t>(hi) << 16);
+      St_hi[bh * D * D + j * D + a] = hi;
+      St_lo[bh * D * D + j * D + a] = to_bf16(s - hif);
+    }
+  } else {
+    z[bh * D + (e - D * D)] = s;
+  }
+}
+
+}  // namespace
+
+KvSplit kv_split(int64_t BH, int64_t N) {
+  // About 512 blocks over the whole problem, 64-token multiples per chunk.
+  const int64_t target_blocks = 512;
+  const int64_t per_head = BH > 0 ? (target_blocks + BH - 1) / BH : 1;
+  int64_t len = (N + per_head - 1) / per_head;
+  len = ((len + kTile - 1) / kTile) * kTile;
+  if (len < kTile) len = kTile;
+  return KvSplit{len, N > 0 ? (N + len - 1) / len : 0};
+}
+
+hipError_t launch_kv_partials(bool bf16, int d, const void* K, const void* V, float* part,
+                              int64_t BH, int64_t N, KvSplit sp, hipStream_t s) {
+  if (sp.chunks == 0 || BH == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(BH * sp.chunks)), block(256);
+  if (bf16) {
+    const bf16_t* k = static_cast<const bf16_t*>(K);
+    const bf16_t* v = static_cast<const bf16_t*>(V);
+    if (d == 128)
+      kv_partials_bf16<128><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+    else
+      kv_partials_bf16<64><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+  } else {
+    const float* k = static_cast<const float*>(K);
+    const float* v = static_cast<const float*>(V);
+    if (d == 128)
+      kv_partials_f32<128><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+    else
+      kv_partials_f32<64><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_reduce(bool bf16, int d, const float* part, float* S, float* z,
+                            uint16_t* St_hi, uint16_t* St_lo, int64_t BH, int64_t chunks,
+                            hipStream_t s) {
+  if (BH == 0) return hipSuccess;
+  const int E = d * d + d;
+  const int bph = (E + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(BH * bph)), block(256);
+  bf16_t* hi = bf16 ? St_hi : nullptr;
+  bf16_t* lo = bf16 ? St_lo : nullptr;
+  if (d == 128)
+    kv_reduce<128><<<grid, block, 0, s>>>(part, S, z, hi, lo, chunks, bph);
+  else
+    kv_reduce<64><<<grid, block, 0, s>>>(part, S, z, hi, lo, chunks, bph);
+  return hipGetLastError();
+}
+
+}  // namespace ha

@@ -1,0 +1,132 @@
+/*
+ * hybrid_attn.h -- C ABI of the MI355X (gfx950) Hybrid Linear-Softmax Attention
+ * library: the gated linear layer, the gated softmax anchor and the 3:1 group
+ * of SANA-Video 2.0 ("SANA-Video 2.0: Hybrid Linear Attention with Attention
+ * Residuals for Efficient Video Generation": summary page, section 03; review
+ * page, sections 1 and 3; news item, "Innovatie in aandachtmechanismen").
+ *
+ * The pages name the two layer kinds and the 3:1 ratio but print no formula.
+ * This library computes, per batch item b and head h, over N tokens:
+ *
+ *   linear:  S = sum_j phi(k_j) v_j^T,  z = sum_j phi(k_j),  phi(x) = max(x, 0)
+ *            o_i = sigmoid(g_i) * (phi(q_i)^T S) / (phi(q_i) . z + HA_LINEAR_EPS)
+ *   softmax: o_i = sigmoid(g_i) * sum_j softmax_j(q_i . k_j / sqrt(d)) v_j
+ *
+ * with sigmoid(x) = 1 / (1 + exp(-x)) and "*" elementwise (G has O's shape).
+ * Attention is bidirectional: every query sees all N tokens of its own (b, h).
+ *
+ * Tensor layout: every Q, K, V, G, O is a dense row-major [B, H, N, d] array,
+ * d fastest; a group takes stacked [4, B, H, N, d] arrays, layer l at element
+ * offset l * B * H * N * d.  All five tensors of a call share one dtype.
+ *
+ * Ownership and ordering: the caller owns every buffer (device memory),
+ * including the workspace.  The library allocates nothing, frees nothing and
+ * keeps no state between calls, so calls are reentrant.  All work is enqueued
+ * asynchronously on `stream` (0 = the null stream) of the current device; inputs
+ * must stay alive and unmodified until the stream has passed the call.
+ *
+ * Errors: every entry point validates its arguments on the host, in the order
+ * listed under ha_status, and returns before any HIP call when they are invalid:
+ * nothing is enqueued.  An empty problem (B, H or N equal to 0) returns HA_OK
+ * and enqueues nothing, except hybrid_attn_kv_state, which still writes a zero
+ * state when B * H > 0.  A failed kernel launch returns HA_EHIP; faults inside
+ * a kernel surface at the caller's next synchronisation of the stream.  No C++
+ * exception crosses this interface.
+ *
+ * Determinism: the split of the linear-state reduction over tokens is a pure
+ * function of (B, H, N, d); partial states are summed in a fixed order without
+ * atomics, so repeated calls on the same inputs give bitwise equal outputs.
+ */
+#ifndef HYBRID_ATTN_H
+#define HYBRID_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HA_API __attribute__((visibility("default")))
+
+/* Storage dtype of Q, K, V, G, O.  HA_BF16: bfloat16 I/O, bf16 MFMA products
+ * with float32 accumulation, outputs rounded to nearest even.  HA_F32: float32
+ * I/O and float32 arithmetic throughout. */
+typedef enum ha_dtype { HA_BF16 = 0, HA_F32 = 1 } ha_dtype;
+
+/* Status codes, in the order the checks run. */
+typedef enum ha_status {
+  HA_OK = 0,
+  HA_EUNSUPPORTED = -2, /* d not 64 or 128, or unknown dtype                      */
+  HA_EINVAL = -1,       /* negative or too large B/H/N, null pointer, output that
+                           overlaps an input, null kinds array                   */
+  HA_EALIGN = -3,       /* a tensor or workspace pointer not 16-byte aligned      */
+  HA_EWORKSPACE = -4,   /* workspace null or smaller than hybrid_attn_workspace_bytes */
+  HA_EHIP = -5          /* a kernel launch or event record failed                 */
+} ha_status;
+
+/* eps of the linear layer's denominator phi(q).z + eps. */
+#define HA_LINEAR_EPS 1e-6f
+
+/* Size limits checked by every entry point (HA_EINVAL beyond them). */
+#define HA_MAX_N (1LL << 24)   /* tokens per (b, h)  */
+#define HA_MAX_BH (1LL << 20)  /* B * H              */
+
+/* Text for a status code (static storage, never NULL). */
+HA_API const char* hybrid_attn_strerror(int status);
+
+/* Bytes of device workspace that hybrid_attn_linear, hybrid_attn_group and
+ * hybrid_attn_kv_state need for these sizes.  Pure function of its arguments:
+ * no device query.  Returns 0 for an empty or invalid problem. */
+HA_API size_t hybrid_attn_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype);
+
+/* Linear-attention state of every (b, h): S[b,h] = sum_j phi(k_j) v_j^T as a
+ * row-major float32 [B, H, d, d] array (row = key feature, column = value
+ * feature) and z[b,h] = sum_j phi(k_j) as float32 [B, H, d].  K, V: [B, H, N, d]
+ * of `dtype`.  This is the first half of the linear layer on its own (its
+ * state reduction); the layer below computes the same state in its workspace. */
+HA_API int hybrid_attn_kv_state(const void* K, const void* V, float* S, float* z,
+                                int B, int H, int64_t N, int d, ha_dtype dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One gated linear-attention layer (formula above).  Q, K, V, G in, O out, all
+ * [B, H, N, d] of `dtype`.  O must not overlap any input. */
+HA_API int hybrid_attn_linear(const void* Q, const void* K, const void* V, const void* G, void* O,
+                              int B, int H, int64_t N, int d, ha_dtype dtype,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One gated softmax anchor layer (formula above), logit scale 1/sqrt(d).  No
+ * workspace.  O must not overlap any input. */
+HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, const void* G, void* O,
+                               int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream);
+
+/* One hybrid group: layers 0, 1, 2 gated linear, layer 3 the gated softmax
+ * anchor (the 3:1 ratio of the pages, anchor last in the period).  Q4, K4, V4,
+ * G4 in and O4 out are stacked [4, B, H, N, d] arrays; layer l of the output is
+ * bitwise equal to the single-layer call on layer l of the inputs.  The three
+ * linear layers reuse one workspace in turn. */
+HA_API int hybrid_attn_group(const void* Q4, const void* K4, const void* V4, const void* G4, void* O4,
+                             int B, int H, int64_t N, int d, ha_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* hybrid_attn_group that also records five caller-created events on `stream`:
+ * events[0] before layer 0 and events[l + 1] after layer l, so the caller can
+ * time each layer of the group with hipEventElapsedTime.  A NULL `events`
+ * behaves exactly like hybrid_attn_group; otherwise all five must be valid
+ * events of the stream's device (HA_EINVAL for a NULL entry). */
+HA_API int hybrid_attn_group_timed(const void* Q4, const void* K4, const void* V4, const void* G4,
+                                   void* O4, int B, int H, int64_t N, int d, ha_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t const events[5]);
+
+/* Writes the layer kinds of a group in order: 0 = gated linear, 1 = gated
+ * softmax anchor; i.e. {0, 0, 0, 1}.  Returns HA_EINVAL for a NULL array. */
+HA_API int hybrid_attn_group_schedule(int kinds[4]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYBRID_ATTN_H */

@@ -1,0 +1,116 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+and rejects bad arguments before any HIP call (no GPU is touched here)."""
+import ctypes
+import subprocess
+
+import pytest
+
+from hybrid_linear_softmax_amd import _lib
+
+HA_BF16, HA_F32 = _lib.HA_BF16, _lib.HA_F32
+OK, EINVAL, EUNSUP, EALIGN, EWS = _lib.HA_OK, _lib.HA_EINVAL, _lib.HA_EUNSUPPORTED, _lib.HA_EALIGN, _lib.HA_EWORKSPACE
+
+# Fake, distinct, 256-byte aligned "device" addresses: validation only compares them.
+GB = 1 << 30
+Q, K, V, G, O, WS, S, Z = (GB * (i + 1) for i in range(8))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _lib.header_functions()
+    assert set(declared) == set(_lib.SIGNATURES), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else leaks out of the library's own code
+    assert {n for n in exported if n.startswith("hybrid_attn_")} == set(declared)
+
+
+def test_strerror_and_schedule(lib):
+    for code in (OK, EINVAL, EUNSUP, EALIGN, EWS, _lib.HA_EHIP, 12345):
+        assert lib.hybrid_attn_strerror(code)
+    kinds = (ctypes.c_int * 4)()
+    assert lib.hybrid_attn_group_schedule(kinds) == OK
+    assert list(kinds) == [0, 0, 0, 1]
+    assert lib.hybrid_attn_group_schedule(None) == EINVAL
+
+
+def test_workspace_is_pure_and_monotone(lib):
+    w = lib.hybrid_attn_workspace_bytes
+    assert w(1, 24, 75600, 128, HA_BF16) == w(1, 24, 75600, 128, HA_BF16)
+    assert w(1, 24, 75600, 128, HA_BF16) > w(1, 24, 75600, 128, HA_F32) > 0
+    assert w(2, 40, 75600, 128, HA_BF16) >= w(1, 40, 75600, 128, HA_BF16)
+    assert w(0, 24, 100, 128, HA_BF16) == 0
+    assert w(1, 24, 100, 96, HA_BF16) == 0
+    assert w(1, 24, -1, 128, HA_BF16) == 0
+    assert w(1, 1, 0, 64, HA_F32) > 0       # an empty sequence still has a (zero) state
+
+
+def _linear(lib, q=Q, k=K, v=V, g=G, o=O, B=1, H=2, N=100, d=64, dt=HA_BF16, ws=WS, nb=None):
+    if nb is None:
+        nb = lib.hybrid_attn_workspace_bytes(B, H, N, d, dt) if B * H > 0 and d in (64, 128) else 0
+    return lib.hybrid_attn_linear(q, k, v, g, o, B, H, N, d, dt, ws, nb, None)
+
+
+def _softmax(lib, q=Q, k=K, v=V, g=G, o=O, B=1, H=2, N=100, d=64, dt=HA_BF16):
+    return lib.hybrid_attn_softmax(q, k, v, g, o, B, H, N, d, dt, None)
+
+
+@pytest.mark.parametrize("call", [_linear, _softmax])
+def test_argument_errors(lib, call):
+    assert call(lib, d=96) == EUNSUP
+    assert call(lib, d=0) == EUNSUP
+    assert call(lib, dt=7) == EUNSUP
+    assert call(lib, B=-1) == EINVAL
+    assert call(lib, N=-5) == EINVAL
+    assert call(lib, N=(1 << 24) + 1) == EINVAL
+    assert call(lib, B=1 << 11, H=1 << 10) == EINVAL
+    assert call(lib, q=None) == EINVAL
+    assert call(lib, o=None) == EINVAL
+    assert call(lib, v=V + 8) == EALIGN
+    assert call(lib, o=O + 2) == EALIGN
+    assert call(lib, o=Q) == EINVAL                 # output aliases an input
+    assert call(lib, o=G + 64 * 16) == EINVAL       # output overlaps the tail of G
+    # empty problems: nothing to do, success, even with null pointers
+    assert call(lib, N=0, q=None, o=None) == OK
+    assert call(lib, B=0) == OK
+    assert call(lib, H=0) == OK
+
+
+def test_workspace_errors(lib):
+    need = lib.hybrid_attn_workspace_bytes(1, 2, 100, 64, HA_BF16)
+    assert _linear(lib, ws=None) == EWS
+    assert _linear(lib, nb=need - 1) == EWS
+    assert _linear(lib, ws=WS + 4) == EALIGN
+    st = lib.hybrid_attn_kv_state(K, V, S, Z, 1, 2, 100, 64, HA_BF16, WS, need - 1, None)
+    assert st == EWS
+    assert lib.hybrid_attn_kv_state(K, V, None, Z, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
+    assert lib.hybrid_attn_kv_state(K, V, S, S + 64, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
+    assert lib.hybrid_attn_kv_state(K, V, K, Z, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
+
+
+def test_group_errors(lib):
+    args = (Q, K, V, G, O, 1, 2, 100, 64, HA_BF16)
+    need = lib.hybrid_attn_workspace_bytes(1, 2, 100, 64, HA_BF16)
+    assert lib.hybrid_attn_group(*args, WS, need - 1, None) == EWS
+    # the group spans 4 layers: an output that overlaps layer 3 of an input is rejected
+    layer_bytes = 1 * 2 * 100 * 64 * 2
+    bad = (Q, K, V, G, G + 3 * layer_bytes, 1, 2, 100, 64, HA_BF16)
+    assert lib.hybrid_attn_group(*bad, WS, need, None) == EINVAL
+    evs = (ctypes.c_void_p * 5)(1, 2, None, 4, 5)
+    assert lib.hybrid_attn_group_timed(*args, WS, need, None, evs) == EINVAL
+    assert lib.hybrid_attn_group(Q, K, V, G, O, 1, 2, 100, 80, HA_BF16, WS, need, None) == EUNSUP
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

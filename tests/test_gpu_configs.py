@@ -1,0 +1,49 @@
+"""The five workloads at their full sizes, run as one hybrid group in the same
+launch configuration the bench times, checked against the oracle on sampled
+heads and query rows (rows are independent, so a sampled row is an exact check)."""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_linear_softmax_amd as ha
+import oracle
+from gpu_util import TOL, check_layer_sampled, rel_err, sample_rows, say
+from workloads import CONFIGS, get, group_inputs_device, heavy_token_positions, layer_inputs_host, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def test_tiny_group_full():
+    w = get("tiny")
+    say("config tiny: full group vs oracle")
+    layers = [layer_inputs_host(w, l, device="cuda") for l in range(4)]
+    x = {k: torch.stack([L[k] for L in layers]).contiguous() for k in "QKVG"}
+    out = ha.hybrid_attn_group(x["Q"], x["K"], x["V"], x["G"])
+    torch.cuda.synchronize()
+    ref = oracle.group(*(to_f64(x[k]) for k in "QKVG"))
+    got = to_f64(out)
+    for l in range(4):
+        err = rel_err(got[l], ref[l])
+        say(f"  layer {l} ({oracle.SCHEDULE[l]}): {err:.2e}")
+        assert err < TOL["f32"]
+
+
+@pytest.mark.parametrize("name", [n for n in CONFIGS if n != "tiny"])
+def test_config_group_sampled(name):
+    w = get(name)
+    say(f"config {name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}: generating inputs")
+    x = group_inputs_device(w, "cuda")
+    ws = torch.empty(ha.workspace_bytes(w.B, w.H, w.N, w.d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    say(f"config {name}: running group")
+    out = ha.hybrid_attn_group(x["Q"], x["K"], x["V"], x["G"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    for l, kind in enumerate(oracle.SCHEDULE):
+        heavy = heavy_token_positions(w, l)[:256]
+        rows = sample_rows(w.N, n_rand=512 if kind == "softmax" else 4096, seed=l, extra=heavy)
+        check_layer_sampled(kind, x["Q"][l], x["K"][l], x["V"][l], x["G"][l], out[l], heads, rows,
+                            TOL[w.dtype], f"{name} layer {l}")
+    del x, out, ws
+    torch.cuda.empty_cache()
