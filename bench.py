@@ -1,0 +1,227 @@
+"""Throughput of one Hybrid Linear-Softmax Attention group on one MI355X.
+
+A step is one hybrid group -- three gated linear layers and one gated softmax
+anchor, all on their own seeded synthetic inputs resident in HBM -- run through
+hybrid_attn_group_timed, which records HIP events between the layers on the
+stream the kernels run on.  The headline workload is the 720p/5s latent shape
+(B=1, H=24, N=75,600 tokens, d=128, bf16).
+
+Prints ONE JSON line: tokens/s over the timed steps, the roofline of the
+dominant kernel (the softmax anchor, MFMA-bound) measured live from those
+events, and the float64 CPU oracle timed on a bounded sample of the same
+workload.  Extra fields: per-layer milliseconds and the all-softmax group
+(four anchors) for the hybrid-vs-softmax speedup.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+ANCHOR_SOURCES = ("hybrid_linear_softmax_amd/csrc/anchor.hip", "hybrid_linear_softmax_amd/csrc/ha_device.h")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "anchor_720p5s_pmc.txt")
+
+
+def anchor_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ANCHOR_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per anchor launch from the committed rocprofv3 PMC summary,
+    or None when it is missing, for another workload, or the kernel has changed
+    since the counters were taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("workload") != workload or vals.get("anchor_source_sha256") != anchor_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, rows_sampled: int):
+    """The oracle as it stands, timed on this host on a sample of the workload:
+    the full linear layer of one (b, h) head, and `rows_sampled` query rows of
+    the softmax anchor of one head (rows are independent, each costs the same),
+    extrapolated to one whole group."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import to_f64
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"],
+                  default=1)
+    q, k, v, g = (to_f64(x[n][0, 0, 0]) for n in "QKVG")
+    t0 = time.perf_counter()
+    oracle.linear_attention(q, k, v, g)
+    t_lin = time.perf_counter() - t0
+    q, k, v, g = (to_f64(x[n][3, 0, 0]) for n in "QKVG")
+    rows = np.random.default_rng(0).choice(w.N, size=min(rows_sampled, w.N), replace=False)
+    t0 = time.perf_counter()
+    oracle.softmax_attention(q, k, v, g, rows=rows)
+    t_rows = time.perf_counter() - t0
+    heads = w.B * w.H
+    t_group = 3 * heads * t_lin + heads * (w.N / rows.size) * t_rows
+    return {
+        "value": w.B * w.N / t_group,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: full linear layer of 1 of {heads} heads ({t_lin:.2f} s) and "
+                   f"{rows.size} of {w.N} softmax query rows of 1 head ({t_rows:.2f} s), extrapolated "
+                   f"to 3 linear + 1 softmax layers over {heads} heads ({t_group:.0f} s per group)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="720p5s", help="workload name (default: the 720p/5s shape)")
+    ap.add_argument("--allsoftmax-steps", type=int, default=3,
+                    help="steps of the all-softmax group (4 anchors) for the speedup ratio; 0 skips")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="softmax rows the oracle baseline samples")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(every (b, h) is independent; see the multi-GPU design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hybrid_linear_softmax_amd as ha
+    from workloads import get, group_inputs_device
+
+    w = get(args.config)
+    if w.dtype != "bf16":
+        raise SystemExit("bench workloads are the bf16 shapes; the fp32 tiny shape is a test case")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}; generating inputs", file=sys.stderr,
+          flush=True)
+    x = group_inputs_device(w, dev)
+    O4 = torch.empty_like(x["Q"])
+    ws = torch.empty(ha.workspace_bytes(w.B, w.H, w.N, w.d, torch.bfloat16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(max(args.steps, 1))]
+
+    def step(i=None):
+        ha.hybrid_attn_group(x["Q"], x["K"], x["V"], x["G"], O4, workspace=ws,
+                             events=None if i is None else evs[i])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    layer_ms = [sum(evs[i][l].elapsed_time(evs[i][l + 1]) for i in range(args.steps)) / args.steps
+                for l in range(4)]
+    tokens_per_s = w.B * w.N * args.steps / (total_ms / 1e3)
+
+    BH = w.B * w.H
+    anchor_ms = layer_ms[3]
+    anchor_flop = 4.0 * BH * w.N * w.N * w.d          # QK^T and PV, 2 flops per multiply-add
+    achieved = anchor_flop / (anchor_ms / 1e3) / 1e12
+    roofline = {
+        "kernel": "anchor_bf16 (gated softmax anchor)",
+        "bound": "mfma",
+        "achieved": round(achieved, 1),
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": measured_traffic(w.name),
+    }
+    lin_ms = sum(layer_ms[:3]) / 3
+    lin_bytes = BH * w.N * w.d * 2 * 5                 # Q, K, V, G read + O written, bf16
+    extra = {
+        "layers_ms": [round(t, 3) for t in layer_ms],
+        "linear_layer_hbm_gbs": round(lin_bytes / (lin_ms / 1e3) / 1e9, 1),
+    }
+
+    if args.allsoftmax_steps > 0:
+        def soft4():
+            for l in range(4):
+                ha.hybrid_attn_softmax(x["Q"][l], x["K"][l], x["V"][l], x["G"][l], O4[l])
+        soft4()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(args.allsoftmax_steps):
+            soft4()
+        a1.record()
+        torch.cuda.synchronize()
+        soft_ms = a0.elapsed_time(a1) / args.allsoftmax_steps
+        extra["allsoftmax_group_ms"] = round(soft_ms, 3)
+        extra["hybrid_speedup_vs_allsoftmax"] = round(soft_ms / ms_per_step, 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, x, args.cpu_rows)
+
+    line = {
+        "metric": "hybrid 3:1 attention group tokens/s at 720p/5s shape; % of bf16 MFMA/HBM peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "layers": "linear,linear,linear,softmax", "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
