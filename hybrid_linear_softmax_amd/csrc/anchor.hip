@@ -4,17 +4,29 @@
 // key blocks stream through LDS and an online maximum and sum per query row
 // rescale the running output (the flash-attention recurrence).
 //
-// bf16 kernel, one block = 128 queries of one (b, h), 4 waves x 32 queries:
+// bf16 kernel: one block = 256 queries of one (b, h), 8 waves x 32 queries
+// (two waves per SIMD), 64 keys per iteration.
 //  * logits are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
 //    the A operand is a K row from LDS, the B operand the wave's Q rows, held in
 //    registers.  A lane's accumulator then holds 16 keys of ONE query, so the
-//    row maximum and sum are mostly lane-local (one exchange with lane ^ 32);
+//    row maximum and sum are lane-local except for one exchange with lane ^ 32;
 //  * the probabilities P^T stay in registers and feed the PV MFMA directly as
 //    its B operand (O^T += V^T P^T).  The key order that the accumulator layout
 //    gives each lane is matched by storing V^T in LDS with bits 2 and 3 of the
 //    key index swapped inside every 16-key group;
-//  * V is transposed on the way into LDS (4 keys x 8 features per thread);
-//  * the next key block's loads are issued before the current block's MFMAs.
+//  * V is transposed on its way into LDS (4 keys x 8 features per thread, one
+//    v_perm per output dword); lanes are assigned so that the transposed 8-byte
+//    stores of a wave fall on distinct LDS banks;
+//  * K and V are read with buffer loads whose record count is the head's size:
+//    rows past N read as zero without any per-load bounds arithmetic;
+//  * K/V tiles are double-buffered in LDS (one barrier per key block) and the
+//    next block's loads are in flight during the current block's MFMAs;
+//  * the running maximum is updated lazily: the output is rescaled only when a
+//    row maximum grows by more than 2^8 in exp2 units (the probabilities stay
+//    below 256, exact enough in fp32 and bf16), which after the first blocks is
+//    almost never;
+//  * row sums are taken over the bf16-rounded probabilities with v_dot2 (two per
+//    instruction), i.e. over exactly the weights the PV product uses.
 #include "ha_device.h"
 #include "ha_launch.h"
 
@@ -22,31 +34,37 @@ namespace ha {
 
 namespace {
 
-constexpr int kBr = 128;  // queries per block
+constexpr int kBr = 256;  // queries per block (8 waves x 32)
 constexpr int kBc = 64;   // keys per iteration
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRescale = 8.0f;  // log2 of the largest unrescaled probability
 
 // LDS column of key k (0..63 inside a key block) in the V^T tile.
 __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
 }
 
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void anchor_bf16(const bf16_t* __restrict__ Q,
+__global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__ Q,
                                                       const bf16_t* __restrict__ K,
                                                       const bf16_t* __restrict__ V,
                                                       const bf16_t* __restrict__ G,
                                                       bf16_t* __restrict__ O, int64_t N,
                                                       int64_t qblocks, int64_t total, float c) {
+  constexpr int NT = 512;
   constexpr int KP = D + 8;              // LDS pitch of K rows (elements)
   constexpr int VP = kBc + 8;            // LDS pitch of V^T rows (elements)
   constexpr int FG = D / 8;              // 16-byte groups per row
-  constexpr int KCH = kBc * FG / 256;    // K chunks per thread per block
+  constexpr int KCH = kBc * FG / NT;     // K chunks per thread per block
   constexpr int VSUB = (kBc / 4) * FG;   // V sub-tiles (4 keys x 8 features) per block
   constexpr int KS = D / 16;             // k-steps of the logit MFMA
   constexpr int RB = D / 32;             // 32-feature row blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16_t sK[kBc * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[D * VP];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][kBc * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[2][D * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -58,6 +76,11 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const bf16_t* __restrict__
   const int64_t q0 = (id % qblocks) * kBr + 32 * wave;
   const int64_t base = bh * N * D;
   const int64_t qrow = q0 + l32;
+  const uint32_t head_bytes = static_cast<uint32_t>(N * D * 2);
+  const __amdgpu_buffer_rsrc_t rK =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, (int)head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rV =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, (int)head_bytes, 0x00020000);
 
   bf16x8 qf[KS];
 #pragma unroll
@@ -65,24 +88,44 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const bf16_t* __restrict__
     qf[s] = as_bf16x8(qrow < N ? *reinterpret_cast<const uint4*>(Q + base + qrow * D + 16 * s + 8 * h)
                                : make_uint4(0, 0, 0, 0));
 
-  // loads of one key block into registers
+  // V sub-tile of this thread: keys 4 v_m .. 4 v_m + 3, features 8 v_fg .. + 7;
+  // consecutive lanes take consecutive key groups (distinct banks on store).
   const bool v_loader = tid < VSUB;
-  const int v_fg = tid % FG, v_m = tid / FG;
+  const int v_fg = tid / 16, v_m = tid % 16;
   uint4 kreg[KCH], vreg[4];
   auto load_block = [&](int64_t k0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int64_t key = k0 + cidx / FG;
-      kreg[i] = key < N ? *reinterpret_cast<const uint4*>(K + base + key * D + 8 * (cidx % FG))
-                        : make_uint4(0, 0, 0, 0);
+      const int cidx = tid + NT * i;
+      kreg[i] = buffer_load16(rK, static_cast<uint32_t>((k0 + cidx / FG) * (D * 2) + (cidx % FG) * 16));
     }
     if (v_loader) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = k0 + 4 * v_m + r;
-        vreg[r] = key < N ? *reinterpret_cast<const uint4*>(V + base + key * D + 8 * v_fg)
-                          : make_uint4(0, 0, 0, 0);
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = buffer_load16(rV, static_cast<uint32_t>((k0 + 4 * v_m + r) * (D * 2) + v_fg * 16));
+    }
+  };
+  auto store_block = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int cidx = tid + NT * i;
+      *reinterpret_cast<uint4*>(&sK[b][(cidx / FG) * KP + 8 * (cidx % FG)]) = kreg[i];
+    }
+    if (v_loader) {
+      const int pos = vt_pos(4 * v_m);
+      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
+      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
+      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
+      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // feature pair (2p, 2p+1) of keys 0..3: low halves, then high halves
+        *reinterpret_cast<uint2*>(&sVt[b][(8 * v_fg + 2 * p) * VP + pos]) =
+            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x05040100u),
+                       __builtin_amdgcn_perm(r3[p], r2[p], 0x05040100u));
+        *reinterpret_cast<uint2*>(&sVt[b][(8 * v_fg + 2 * p + 1) * VP + pos]) =
+            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u),
+                       __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
       }
     }
   };
@@ -95,26 +138,7 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const bf16_t* __restrict__
   float m = -INFINITY;  // running max of the raw logits of this lane's query
   float lsum = 0.f;     // running sum of this lane's probabilities (half the keys)
 
-  const int64_t nkb = (N + kBc - 1) / kBc;
-  load_block(0);
-  for (int64_t kb = 0; kb < nkb; ++kb) {
-    const int64_t k0 = kb * kBc;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + 256 * i;
-      *reinterpret_cast<uint4*>(sK + (cidx / FG) * KP + 8 * (cidx % FG)) = kreg[i];
-    }
-    if (v_loader) {
-      uint2 tr[8];
-      transpose4x8(vreg, tr);
-      const int pos = vt_pos(4 * v_m);
-#pragma unroll
-      for (int f = 0; f < 8; ++f) *reinterpret_cast<uint2*>(sVt + (8 * v_fg + f) * VP + pos) = tr[f];
-    }
-    __syncthreads();
-    if (kb + 1 < nkb) load_block(k0 + kBc);
-
+  auto compute = [&](int b, int64_t k0) {
     // S^T for 64 keys x 32 queries: two 32x32 blocks
     f32x16 s[2];
 #pragma unroll
@@ -123,18 +147,18 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const bf16_t* __restrict__
       for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (32 * t + l32) * KP + 16 * st + 8 * h);
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&sK[b][(32 * t + l32) * KP + 16 * st + 8 * h]);
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[t], 0, 0, 0);
       }
     }
     if (k0 + kBc > N) {  // ragged last block: keys >= N get -inf
+      const int lim = static_cast<int>(N - k0);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= N) s[t][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * t + 8 * (r >> 2) + 4 * h + (r & 3) >= lim) s[t][r] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
@@ -142,11 +166,18 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const bf16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-    const float mc = m_new * c;
-    m = m_new;
-    float ps = 0.f;
+    if (__any((mx - m) * c > kLazyRescale)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[rb][r] *= alpha;
+    }
+    const float mc = m * c;
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     bf16x8 pf[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -154,31 +185,39 @@ __global__ __launch_bounds__(256, 2) void anchor_bf16(const bf16_t* __restrict__
       for (int tt = 0; tt < 2; ++tt) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * tt + j], c, -mc));
-          ps += p[j];
-        }
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * tt + j], c, -mc));
         uint4 pk;
         pk.x = pack_bf16(p[0], p[1]);
         pk.y = pack_bf16(p[2], p[3]);
         pk.z = pack_bf16(p[4], p[5]);
         pk.w = pack_bf16(p[6], p[7]);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.x), one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.y), one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.z), one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.w), one, lsum, false);
         pf[t][tt] = as_bf16x8(pk);
       }
-    lsum = fmaf(lsum, alpha, ps);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[rb][r] *= alpha;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(sVt + (32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+              &sVt[b][(32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h]);
           o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][tt], o[rb], 0, 0, 0);
         }
-    }
+  };
+
+  const int64_t nkb = (N + kBc - 1) / kBc;
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) load_block((kb + 1) * kBc);
+    compute(static_cast<int>(kb & 1), kb * kBc);
+    if (kb + 1 < nkb) store_block(static_cast<int>((kb + 1) & 1));
+    __syncthreads();
   }
 
   const float l = lsum + __shfl_xor(lsum, 32);
@@ -281,7 +320,7 @@ hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const v
     const bf16_t* v = static_cast<const bf16_t*>(V);
     const bf16_t* g = static_cast<const bf16_t*>(G);
     bf16_t* o = static_cast<bf16_t*>(O);
-    const dim3 grid(static_cast<unsigned>(total)), block(256);
+    const dim3 grid(static_cast<unsigned>(total)), block(512);
     if (d == 128)
       anchor_bf16<128><<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, total, c);
     else

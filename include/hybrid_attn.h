@@ -71,7 +71,7 @@ typedef enum ha_status {
 #define HA_LINEAR_EPS 1e-6f
 
 /* Size limits checked by every entry point (HA_EINVAL beyond them). */
-#define HA_MAX_N (1LL << 24)   /* tokens per (b, h)  */
+#define HA_MAX_N (1LL << 23)   /* tokens per (b, h); byte offsets of one head fit 32 bits */
 #define HA_MAX_BH (1LL << 20)  /* B * H              */
 
 /* Text for a status code (static storage, never NULL). */

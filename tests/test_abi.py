@@ -70,7 +70,7 @@ def test_argument_errors(lib, call):
     assert call(lib, dt=7) == EUNSUP
     assert call(lib, B=-1) == EINVAL
     assert call(lib, N=-5) == EINVAL
-    assert call(lib, N=(1 << 24) + 1) == EINVAL
+    assert call(lib, N=(1 << 23) + 1) == EINVAL
     assert call(lib, B=1 << 11, H=1 << 10) == EINVAL
     assert call(lib, q=None) == EINVAL
     assert call(lib, o=None) == EINVAL

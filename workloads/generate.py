@@ -102,8 +102,7 @@ def layer_inputs_device(w: Workload, layer: int = 0, device="cuda", *, out=None)
                 if _mean(w, name) != 0.0:
                     x.add_(_mean(w, name))
                 if name in ("K", "V") and heavy_t is not None:
-                    x.index_mul_(0, heavy_t, torch.full((heavy_t.numel(), 1), w.heavy_scale,
-                                                        device=device).expand(-1, w.d).contiguous())
+                    x[heavy_t] *= w.heavy_scale
                 t[b, h].copy_(x)
                 del x
         res[name] = t
