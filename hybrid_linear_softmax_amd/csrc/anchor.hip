@@ -19,14 +19,18 @@
 //    stores of a wave fall on distinct LDS banks;
 //  * K and V are read with buffer loads whose record count is the head's size:
 //    rows past N read as zero without any per-load bounds arithmetic;
-//  * K/V tiles are double-buffered in LDS (one barrier per key block) and the
-//    next block's loads are in flight during the current block's MFMAs;
+//  * software pipeline: the logit MFMAs of key block j+1 are issued while the
+//    softmax of block j runs on the VALU (same wave); K and V tiles are double-
+//    buffered in LDS, K one block ahead of V, one barrier per key block, and
+//    the loads of the next tiles are in flight during the MFMAs;
 //  * the running maximum is updated lazily: the output is rescaled only when a
 //    row maximum grows by more than 2^8 in exp2 units (the probabilities stay
 //    below 256, exact enough in fp32 and bf16), which after the first blocks is
 //    almost never;
 //  * row sums are taken over the bf16-rounded probabilities with v_dot2 (two per
 //    instruction), i.e. over exactly the weights the PV product uses.
+#include <type_traits>
+
 #include "ha_device.h"
 #include "ha_launch.h"
 
@@ -93,42 +97,6 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   const bool v_loader = tid < VSUB;
   const int v_fg = tid / 16, v_m = tid % 16;
   uint4 kreg[KCH], vreg[4];
-  auto load_block = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + NT * i;
-      kreg[i] = buffer_load16(rK, static_cast<uint32_t>((k0 + cidx / FG) * (D * 2) + (cidx % FG) * 16));
-    }
-    if (v_loader) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = buffer_load16(rV, static_cast<uint32_t>((k0 + 4 * v_m + r) * (D * 2) + v_fg * 16));
-    }
-  };
-  auto store_block = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + NT * i;
-      *reinterpret_cast<uint4*>(&sK[b][(cidx / FG) * KP + 8 * (cidx % FG)]) = kreg[i];
-    }
-    if (v_loader) {
-      const int pos = vt_pos(4 * v_m);
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        // feature pair (2p, 2p+1) of keys 0..3: low halves, then high halves
-        *reinterpret_cast<uint2*>(&sVt[b][(8 * v_fg + 2 * p) * VP + pos]) =
-            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x05040100u),
-                       __builtin_amdgcn_perm(r3[p], r2[p], 0x05040100u));
-        *reinterpret_cast<uint2*>(&sVt[b][(8 * v_fg + 2 * p + 1) * VP + pos]) =
-            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u),
-                       __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
-      }
-    }
-  };
 
   f32x16 o[RB];
 #pragma unroll
@@ -138,34 +106,40 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   float m = -INFINITY;  // running max of the raw logits of this lane's query
   float lsum = 0.f;     // running sum of this lane's probabilities (half the keys)
 
-  auto compute = [&](int b, int64_t k0) {
-    // S^T for 64 keys x 32 queries: two 32x32 blocks
-    f32x16 s[2];
+  // Software pipeline over 64-key blocks j: each step issues the logit MFMAs of
+  // block j+1 (independent work) while the softmax of block j runs on the VALU,
+  // then the PV MFMAs of block j.  K runs one block ahead of V in separate
+  // double buffers.  The loop is unrolled by two so the two logit tiles swap
+  // roles without register copies, and only the last steps carry the mask.
+  auto qk = [&](int b, f32x16 (&s)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&sK[b][(32 * t + l32) * KP + 16 * st + 8 * h]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[b][(32 * t + l32) * KP + 16 * st + 8 * h]);
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[t], 0, 0, 0);
       }
     }
-    if (k0 + kBc > N) {  // ragged last block: keys >= N get -inf
-      const int lim = static_cast<int>(N - k0);
+  };
+  auto mask = [&](f32x16 (&s)[2], int64_t k0) {
+    const int lim = static_cast<int>(max((int64_t)0, N - k0));
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * t + 8 * (r >> 2) + 4 * h + (r & 3) >= lim) s[t][r] = -INFINITY;
-    }
+      for (int r = 0; r < 16; ++r)
+        if (32 * t + 8 * (r >> 2) + 4 * h + (r & 3) >= lim) s[t][r] = -INFINITY;
+  };
+  auto rowmax = [&](const f32x16 (&s)[2]) {
     float mx = s[0][0];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+  auto rescale = [&](float mx) {
     if (__any((mx - m) * c > kLazyRescale)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
@@ -176,9 +150,10 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[rb][r] *= alpha;
     }
+  };
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  auto softmax_p = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2]) {
     const float mc = m * c;
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    bf16x8 pf[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -187,37 +162,105 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * tt + j], c, -mc));
         uint4 pk;
-        pk.x = pack_bf16(p[0], p[1]);
-        pk.y = pack_bf16(p[2], p[3]);
-        pk.z = pack_bf16(p[4], p[5]);
-        pk.w = pack_bf16(p[6], p[7]);
+        pk.x = pack_bf16(p[0], p[1]); pk.y = pack_bf16(p[2], p[3]);
+        pk.z = pack_bf16(p[4], p[5]); pk.w = pack_bf16(p[6], p[7]);
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.x), one, lsum, false);
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.y), one, lsum, false);
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.z), one, lsum, false);
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.w), one, lsum, false);
         pf[t][tt] = as_bf16x8(pk);
       }
+  };
+  auto pv = [&](int b, const bf16x8 (&pf)[2][2]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-              &sVt[b][(32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h]);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sVt[b][(32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h]);
           o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][tt], o[rb], 0, 0, 0);
         }
   };
-
-  const int64_t nkb = (N + kBc - 1) / kBc;
-  load_block(0);
-  store_block(0);
+  // K and V use separate double buffers; K runs one block ahead of V:
+  // step j reads K_{j+1} (buffer (j+1)&1) and V_j (buffer j&1) and stores
+  // K_{j+2} into K buffer j&1 and V_{j+1} into V buffer (j+1)&1.
+  auto load_k = [&](int64_t kk0) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int cidx = tid + NT * i;
+      kreg[i] = buffer_load16(rK, static_cast<uint32_t>((kk0 + cidx / FG) * (D * 2) + (cidx % FG) * 16));
+    }
+  };
+  auto load_v = [&](int64_t vk0) {
+    if (v_loader) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = buffer_load16(rV, static_cast<uint32_t>((vk0 + 4 * v_m + r) * (D * 2) + v_fg * 16));
+    }
+  };
+  auto store_kv = [&](int kb, int vb) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int cidx = tid + NT * i;
+      *reinterpret_cast<uint4*>(&sK[kb][(cidx / FG) * KP + 8 * (cidx % FG)]) = kreg[i];
+    }
+    if (v_loader) {
+      const int pos = vt_pos(4 * v_m);
+      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
+      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
+      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
+      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        *reinterpret_cast<uint2*>(&sVt[vb][(8 * v_fg + 2 * p) * VP + pos]) =
+            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x05040100u), __builtin_amdgcn_perm(r3[p], r2[p], 0x05040100u));
+        *reinterpret_cast<uint2*>(&sVt[vb][(8 * v_fg + 2 * p + 1) * VP + pos]) =
+            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u), __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
+      }
+    }
+  };
+  // prologue: K_0, V_0 -> buffers 0, K_1 -> K buffer 1; S_0
+  load_k(0);
+  load_v(0);
+  store_kv(0, 0);
+  load_k(kBc);
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int cidx = tid + NT * i;
+    *reinterpret_cast<uint4*>(&sK[1][(cidx / FG) * KP + 8 * (cidx % FG)]) = kreg[i];
+  }
   __syncthreads();
-  for (int64_t kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) load_block((kb + 1) * kBc);
-    compute(static_cast<int>(kb & 1), kb * kBc);
-    if (kb + 1 < nkb) store_block(static_cast<int>((kb + 1) & 1));
+  f32x16 sa[2], sb[2];
+  qk(0, sa);
+  if (kBc > N) mask(sa, 0);
+  m = rowmax(sa);
+  __syncthreads();
+  auto step = [&](int64_t j, f32x16 (&scur)[2], f32x16 (&snext)[2], auto masked) {
+    load_k((j + 2) * kBc);
+    bf16x8 pf[2][2];
+    qk(static_cast<int>((j + 1) & 1), snext);
+    softmax_p(scur, pf);
+    load_v((j + 1) * kBc);  // V is stored at the end of the step: short live range
+    if (decltype(masked)::value) mask(snext, (j + 1) * kBc);
+    pv(static_cast<int>(j & 1), pf);
+    const float mx = rowmax(snext);
+    store_kv(static_cast<int>(j & 1), static_cast<int>((j + 1) & 1));
+    rescale(mx);
     __syncthreads();
+  };
+  using NoMask = std::integral_constant<bool, false>;
+  using Mask = std::integral_constant<bool, true>;
+  const int64_t nkb = (N + kBc - 1) / kBc;
+  const int64_t nfull = N / kBc;  // blocks 0 .. nfull-1 hold 64 valid keys
+  int64_t j = 0;
+  for (; j + 2 < nfull; j += 2) {
+    step(j, sa, sb, NoMask{});
+    step(j + 1, sb, sa, NoMask{});
+  }
+  for (; j < nkb; j += 2) {
+    step(j, sa, sb, Mask{});
+    if (j + 1 < nkb) step(j + 1, sb, sa, Mask{});
   }
 
   const float l = lsum + __shfl_xor(lsum, 32);

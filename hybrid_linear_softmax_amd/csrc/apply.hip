@@ -63,20 +63,31 @@ __global__ __launch_bounds__(256) void apply_bf16(const bf16_t* __restrict__ Q,
   const int64_t ntiles = (N + kTok - 1) / kTok;
   const int64_t tb = blk * tiles_per_block;
   const int64_t te = min(ntiles, tb + tiles_per_block);
-  for (int64_t t = tb; t < te; ++t) {
-    const int64_t tok0 = t * kTok;
-    uint4 gv[CH];
+
+  // Q and G chunks of one tile: chunk c = tid + 256 i -> token c / FG, features
+  // 8 (c % FG) .. + 7 (the feature group is the same for every chunk of a thread)
+  uint4 qv[CH], gv[CH];
+  auto load_tile = [&](int64_t t) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / FG;
-      const int64_t tok = tok0 + row;
-      uint4 q = make_uint4(0, 0, 0, 0);
+      const int64_t tok = t * kTok + (tid + 256 * i) / FG;
+      qv[i] = make_uint4(0, 0, 0, 0);
       gv[i] = make_uint4(0, 0, 0, 0);
-      if (tok < N) {
-        q = relu8(*reinterpret_cast<const uint4*>(Q + base + tok * D + 8 * fg));
+      if (t < te && tok < N) {
+        qv[i] = *reinterpret_cast<const uint4*>(Q + base + tok * D + 8 * fg);
         gv[i] = *reinterpret_cast<const uint4*>(G + base + tok * D + 8 * fg);
       }
+    }
+  };
+  load_tile(tb);
+  for (int64_t t = tb; t < te; ++t) {
+    const int64_t tok0 = t * kTok;
+    uint4 gcur[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int row = (tid + 256 * i) / FG;
+      const uint4 q = relu8(qv[i]);
+      gcur[i] = gv[i];
       float dp = bf_lo(q.x) * zf[0];
       dp = fmaf(bf_hi(q.x), zf[1], dp);
       dp = fmaf(bf_lo(q.y), zf[2], dp);
@@ -91,6 +102,7 @@ __global__ __launch_bounds__(256) void apply_bf16(const bf16_t* __restrict__ Q,
       if (fg == 0) sDen[row] = dp + eps;
     }
     __syncthreads();
+    load_tile(t + 1);  // next tile's Q and G stream in during this tile's MFMAs
 #pragma unroll
     for (int mb = 0; mb < kTok / 16; ++mb) {
       f32x4 acc[NB];
@@ -115,18 +127,18 @@ __global__ __launch_bounds__(256) void apply_bf16(const bf16_t* __restrict__ Q,
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / FG;
+      const int row = (tid + 256 * i) / FG;
       const int64_t tok = tok0 + row;
       if (tok < N) {
         const float4 n0 = *reinterpret_cast<const float4*>(sNum + row * NP + 8 * fg);
         const float4 n1 = *reinterpret_cast<const float4*>(sNum + row * NP + 8 * fg + 4);
         const float inv = __builtin_amdgcn_rcpf(sDen[row]);
+        const uint4 g = gcur[i];
         uint4 o;
-        o.x = pack_bf16(gate_fast(bf_lo(gv[i].x)) * n0.x * inv, gate_fast(bf_hi(gv[i].x)) * n0.y * inv);
-        o.y = pack_bf16(gate_fast(bf_lo(gv[i].y)) * n0.z * inv, gate_fast(bf_hi(gv[i].y)) * n0.w * inv);
-        o.z = pack_bf16(gate_fast(bf_lo(gv[i].z)) * n1.x * inv, gate_fast(bf_hi(gv[i].z)) * n1.y * inv);
-        o.w = pack_bf16(gate_fast(bf_lo(gv[i].w)) * n1.z * inv, gate_fast(bf_hi(gv[i].w)) * n1.w * inv);
+        o.x = pack_bf16(gate_fast(bf_lo(g.x)) * n0.x * inv, gate_fast(bf_hi(g.x)) * n0.y * inv);
+        o.y = pack_bf16(gate_fast(bf_lo(g.y)) * n0.z * inv, gate_fast(bf_hi(g.y)) * n0.w * inv);
+        o.z = pack_bf16(gate_fast(bf_lo(g.z)) * n1.x * inv, gate_fast(bf_hi(g.z)) * n1.y * inv);
+        o.w = pack_bf16(gate_fast(bf_lo(g.w)) * n1.z * inv, gate_fast(bf_hi(g.w)) * n1.w * inv);
         *reinterpret_cast<uint4*>(O + base + tok * D + 8 * fg) = o;
       }
     }
@@ -187,8 +199,10 @@ hipError_t launch_apply(bool bf16, int d, const void* Q, const void* G, void* O,
   if (BH == 0 || N == 0) return hipSuccess;
   const int tile = bf16 ? kTok : 16;
   const int64_t ntiles = (N + tile - 1) / tile;
-  // About 1024 blocks in all; each walks a contiguous run of tiles of one head.
-  int64_t bph = (1024 + BH - 1) / BH;
+  // About 2048 blocks (several per CU, so HBM streams stay busy while blocks
+  // start and finish), each walking a contiguous run of tiles of one head.  The
+  // apply has no cross-block reduction: the grid does not affect the result.
+  int64_t bph = (2048 + BH - 1) / BH;
   if (bph > ntiles) bph = ntiles;
   const int64_t tpb = (ntiles + bph - 1) / bph;
   bph = (ntiles + tpb - 1) / tpb;

@@ -45,7 +45,10 @@ __global__ __launch_bounds__(256) void kv_partials_bf16(const bf16_t* __restrict
   const bf16_t* Kh = K + bh * N * D;
   const bf16_t* Vh = V + bh * N * D;
 
-  // sub-tile u of this thread: tensor u / SUB, feature group, 4-token group
+  // sub-tile u of this thread: tensor u / SUB, feature group, 4-token group.
+  // The token group is the fast index across lanes: the transposed 8-byte LDS
+  // stores of 16 consecutive lanes then fill one 128-byte row segment (distinct
+  // banks), while each 64-byte piece of a token row is still read by 4 lanes.
   int sub_fg[PER], sub_m[PER];
   bool sub_k[PER];
 #pragma unroll
@@ -53,8 +56,8 @@ __global__ __launch_bounds__(256) void kv_partials_bf16(const bf16_t* __restrict
     const int u = tid + 256 * i;
     sub_k[i] = u < SUB;
     const int w = u % SUB;
-    sub_fg[i] = w % FG;
-    sub_m[i] = w / FG;
+    sub_fg[i] = w / (kTile / 4);
+    sub_m[i] = w % (kTile / 4);
   }
 
   uint4 regs[PER][4];
@@ -264,8 +267,10 @@ __global__ __launch_bounds__(256) void kv_reduce(const float* __restrict__ part,
 }  // namespace
 
 KvSplit kv_split(int64_t BH, int64_t N) {
-  // About 512 blocks over the whole problem, 64-token multiples per chunk.
-  const int64_t target_blocks = 512;
+  // About 768 blocks over the whole problem (three resident per CU on a 256-CU
+  // part), 64-token multiples per chunk.  A constant, never a device query: the
+  // split fixes the order of the reduction and therefore the result.
+  const int64_t target_blocks = 768;
   const int64_t per_head = BH > 0 ? (target_blocks + BH - 1) / BH : 1;
   int64_t len = (N + per_head - 1) / per_head;
   len = ((len + kTile - 1) / kTile) * kTile;
