@@ -4,6 +4,10 @@ the bench's CPU-baseline leg use it; the library path never does."""
 from .hybrid_ref import (  # noqa: F401
     EPS,
     SCHEDULE,
+    SPARSE_BLOCK_Q,
+    SPARSE_BLOCK_K,
+    allowed_keys,
+    softmax_attention_blocksparse,
     phi,
     sigmoid,
     kv_state,

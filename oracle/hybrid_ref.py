@@ -33,6 +33,10 @@ import numpy as np
 
 EPS = 1e-6
 SCHEDULE = ("linear", "linear", "linear", "softmax")
+# Block-sparse anchor: a pattern lists, for every block of SPARSE_BLOCK_Q
+# consecutive queries, the blocks of SPARSE_BLOCK_K consecutive keys it sees.
+SPARSE_BLOCK_Q = 256
+SPARSE_BLOCK_K = 64
 
 
 def phi(x):
@@ -106,6 +110,43 @@ def softmax_attention(Q, K, V, G, rows=None, row_block=512):
         p = np.exp(logits - m)
         l = p.sum(axis=1, keepdims=True)
         out[s:s + r.size] = sigmoid(G[r]) * (p @ V) / l
+    return out
+
+
+def allowed_keys(N, offsets, indices, qb, block_k=SPARSE_BLOCK_K):
+    """Sorted key positions that query block qb may attend to: the union of the
+    listed key blocks, each clipped to [0, N); indices outside [0, ceil(N/block_k))
+    are ignored and a block listed twice counts once."""
+    nkb = -(-N // block_k)
+    beg, end = int(offsets[qb]), int(offsets[qb + 1])
+    blocks = sorted({int(b) for b in indices[beg:end] if 0 <= int(b) < nkb})
+    if not blocks:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate([np.arange(b * block_k, min((b + 1) * block_k, N)) for b in blocks])
+
+
+def softmax_attention_blocksparse(Q, K, V, G, offsets, indices, rows=None,
+                                  block_q=SPARSE_BLOCK_Q, block_k=SPARSE_BLOCK_K):
+    """Gated softmax attention where query i sees only the keys of the blocks its
+    query block (i // block_q) lists -- the block-sparse form of the anchor that
+    the long-sequence pages point to (Sol-Engine's sparse attention, LoSA's and
+    LVSA's block patterns).  o_i = sigmoid(g_i) * sum_{j in A(i)} softmax_j(q_i.k_j
+    / sqrt(d)) v_j; a query whose set A(i) is empty gets o_i = 0."""
+    Q, K, V, G = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, G))
+    N, d = Q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, V.shape[1]), dtype=np.float64)
+    scale = 1.0 / math.sqrt(d)
+    for qb in np.unique(rows // block_q):
+        sel = np.nonzero(rows // block_q == qb)[0]
+        keys = allowed_keys(N, offsets, indices, qb, block_k)
+        if keys.size == 0:
+            continue
+        r = rows[sel]
+        logits = (Q[r] @ K[keys].T) * scale
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        out[sel] = sigmoid(G[r]) * (p @ V[keys]) / p.sum(axis=1, keepdims=True)
     return out
 
 

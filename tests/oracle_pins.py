@@ -226,6 +226,75 @@ def pin_group_structure(impl):
             assert _rel(out[l, 0, h], ref) < 1e-12, ("group layer", l, h)
 
 
+# ----------------------------------------------------------------------------- block-sparse anchor
+
+def _csr(lists):
+    offsets = np.cumsum([0] + [len(l) for l in lists]).astype(np.int32)
+    indices = np.asarray([b for l in lists for b in l], dtype=np.int32)
+    return offsets, indices
+
+
+def pin_sparse_full_pattern_is_dense(impl):
+    for seed, (N, d) in enumerate([(300, 16), (700, 32)]):
+        Q, K, V, G = _rand(80 + seed, N, d, scale=2.0)
+        nqb, nkb = -(-N // impl.SPARSE_BLOCK_Q), -(-N // impl.SPARSE_BLOCK_K)
+        off, idx = _csr([list(range(nkb))] * nqb)
+        got = impl.softmax_attention_blocksparse(Q, K, V, G, off, idx)
+        assert _rel(got, impl.softmax_attention(Q, K, V, G)) < 1e-13
+
+
+def pin_sparse_matches_masked_library(impl):
+    N, d = 600, 16
+    Q, K, V, G = _rand(90, N, d, scale=2.0)
+    r = _rng(91)
+    nqb, nkb = -(-N // impl.SPARSE_BLOCK_Q), -(-N // impl.SPARSE_BLOCK_K)
+    lists = [sorted(r.choice(nkb, size=int(r.integers(0, nkb + 1)), replace=False).tolist()) for _ in range(nqb)]
+    lists[1] = []                                  # an empty row set
+    off, idx = _csr(lists)
+    mask = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        for b in lists[i // impl.SPARSE_BLOCK_Q]:
+            mask[i, b * impl.SPARSE_BLOCK_K:min(N, (b + 1) * impl.SPARSE_BLOCK_K)] = True
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x)[None, None] for x in (Q, K, V)), attn_mask=torch.from_numpy(mask)[None, None])[0, 0].numpy()
+    ref = ref / (1.0 + np.exp(-G))
+    got = impl.softmax_attention_blocksparse(Q, K, V, G, off, idx)
+    live = mask.any(axis=1)
+    assert np.all(got[~live] == 0.0), "a query with no allowed key gets 0"
+    assert _rel(got[live], ref[live]) < 1e-12
+
+
+def pin_sparse_single_block_and_tail(impl):
+    N, d = 530, 8                                    # last key block holds 530 - 8*64 = 18 keys
+    Q, K, V, G = _rand(95, N, d)
+    nqb, nkb = -(-N // impl.SPARSE_BLOCK_Q), -(-N // impl.SPARSE_BLOCK_K)
+    lists = [[3], [nkb - 1], [0]]
+    off, idx = _csr(lists)
+    got = impl.softmax_attention_blocksparse(Q, K, V, G, off, idx)
+    for qb, (b,) in enumerate(lists):
+        rows = slice(qb * 256, min(N, (qb + 1) * 256))
+        keys = slice(b * 64, min(N, (b + 1) * 64))
+        # queries of block qb against only that key slice: plain softmax attention
+        Qs, Gs = Q[rows], G[rows]
+        Kb, Vb = K[keys], V[keys]
+        s = Qs @ Kb.T / math.sqrt(d)
+        w = np.exp(s - s.max(1, keepdims=True))
+        ref = (w @ Vb) / w.sum(1, keepdims=True) / (1.0 + np.exp(-Gs))
+        assert _rel(got[rows], ref) < 1e-13, ("single block", qb, b)
+
+
+def pin_sparse_set_semantics(impl):
+    N, d = 520, 8
+    Q, K, V, G = _rand(97, N, d)
+    base = [[0, 2, 5], [1, 3], [8]]
+    off, idx = _csr(base)
+    o = impl.softmax_attention_blocksparse(Q, K, V, G, off, idx)
+    off2, idx2 = _csr([[5, 0, 2, 2], [3, 1, 99, -4], [8, 8]])   # reordered, repeated, out of range
+    assert _rel(impl.softmax_attention_blocksparse(Q, K, V, G, off2, idx2), o) < 1e-15
+    rows = np.array([0, 255, 256, 511, 519])
+    assert _rel(impl.softmax_attention_blocksparse(Q, K, V, G, off, idx, rows=rows), o[rows]) < 1e-15
+
+
 ALL_PINS = [
     pin_linear_matches_pairwise_loops,
     pin_linear_state_equals_bruteforce,
@@ -239,4 +308,8 @@ ALL_PINS = [
     pin_softmax_invariances,
     pin_softmax_golden,
     pin_group_structure,
+    pin_sparse_full_pattern_is_dense,
+    pin_sparse_matches_masked_library,
+    pin_sparse_single_block_and_tail,
+    pin_sparse_set_semantics,
 ]

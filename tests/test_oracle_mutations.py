@@ -13,7 +13,8 @@ from oracle import hybrid_ref as R
 
 def _impl(**over):
     ns = {k: getattr(R, k) for k in ("EPS", "SCHEDULE", "phi", "sigmoid", "kv_state", "linear_attention",
-                                     "linear_attention_bruteforce", "softmax_attention", "group", "layer")}
+                                     "linear_attention_bruteforce", "softmax_attention", "group", "layer",
+                                     "SPARSE_BLOCK_Q", "SPARSE_BLOCK_K", "softmax_attention_blocksparse")}
     ns.update(over)
     impl = types.SimpleNamespace(**ns)
 
@@ -90,6 +91,31 @@ def _bad_bruteforce_no_eps(Q, K, V, G, eps=R.EPS):
     return R.linear_attention_bruteforce(Q, K, V, G, eps=0.0)
 
 
+def _sparse_with(key_block=None, query_block=None, drop_tail=False, empty_uniform=False):
+    def sp(Q, K, V, G, offsets, indices, rows=None, block_q=R.SPARSE_BLOCK_Q, block_k=R.SPARSE_BLOCK_K):
+        Q, K, V, G = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, G))
+        N, d = Q.shape
+        rows = np.arange(N) if rows is None else np.asarray(rows)
+        bq = query_block or block_q
+        bk = key_block or block_k
+        out = np.zeros((rows.size, V.shape[1]))
+        for n, i in enumerate(rows):
+            qb = min(i // bq, len(offsets) - 2)
+            blocks = sorted({int(b) for b in indices[offsets[qb]:offsets[qb + 1]] if 0 <= b < -(-N // block_k)})
+            keys = [k for b in blocks for k in range(b * bk, (b + 1) * bk) if (k < N or not drop_tail) and k < N + (0 if not drop_tail else 0)]
+            if drop_tail:
+                keys = [k for k in keys if k < (N // bk) * bk]
+            if not keys:
+                out[n] = (1.0 / (1.0 + np.exp(-G[i]))) / V.shape[1] if empty_uniform else 0.0
+                continue
+            keys = np.asarray(keys)
+            s = Q[i] @ K[keys].T / math.sqrt(d)
+            w = np.exp(s - s.max())
+            out[n] = (1.0 / (1.0 + np.exp(-G[i]))) * (w @ V[keys]) / w.sum()
+        return out
+    return sp
+
+
 MUTANTS = {
     "S transposed": dict(linear_attention=_linear_with(kv=_kv_transposed)),
     "phi applied to V": dict(linear_attention=_linear_with(kv=_kv_phi_on_v)),
@@ -110,6 +136,10 @@ MUTANTS = {
     "anchor first in the period": dict(SCHEDULE=("softmax", "linear", "linear", "linear")),
     "all-linear group": dict(SCHEDULE=("linear", "linear", "linear", "linear")),
     "2:2 group": dict(SCHEDULE=("linear", "softmax", "linear", "softmax")),
+    "sparse: key blocks of 32": dict(softmax_attention_blocksparse=_sparse_with(key_block=32)),
+    "sparse: query blocks of 128": dict(softmax_attention_blocksparse=_sparse_with(query_block=128)),
+    "sparse: ragged key tail dropped": dict(softmax_attention_blocksparse=_sparse_with(drop_tail=True)),
+    "sparse: empty rows not zero": dict(softmax_attention_blocksparse=_sparse_with(empty_uniform=True)),
 }
 
 
