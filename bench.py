@@ -11,6 +11,11 @@ dominant kernel (the softmax anchor, MFMA-bound) measured live from those
 events, and the float64 CPU oracle timed on a bounded sample of the same
 workload.  Extra fields: per-layer milliseconds and the all-softmax group
 (four anchors) for the hybrid-vs-softmax speedup.
+
+--anchor lvsa runs the long-video form instead: the anchor is the block-sparse
+kernel over the LVSA frame pattern of the workload's latent grid (a window of
+frames plus periodic global frames), the three linear layers unchanged; the
+extra field then compares against one dense anchor on the same inputs.
 """
 import argparse
 import hashlib
@@ -25,7 +30,10 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 ANCHOR_SOURCES = ("hybrid_linear_softmax_amd/csrc/anchor.hip", "hybrid_linear_softmax_amd/csrc/ha_device.h")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "anchor_720p5s_pmc.txt")
+
+
+def pmc_summary_path(label: str) -> str:
+    return os.path.join(ROOT, "profiles", f"anchor_{label}_pmc.txt")
 
 
 def anchor_source_hash() -> str:
@@ -36,19 +44,20 @@ def anchor_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(label: str):
     """HBM bytes per anchor launch from the committed rocprofv3 PMC summary,
     or None when it is missing, for another workload, or the kernel has changed
     since the counters were taken."""
-    if not os.path.exists(PMC_SUMMARY):
+    path = pmc_summary_path(label)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("workload") != workload or vals.get("anchor_source_sha256") != anchor_source_hash():
+    if vals.get("workload") != label or vals.get("anchor_source_sha256") != anchor_source_hash():
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -56,11 +65,12 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, x, rows_sampled: int):
+def cpu_baseline(w, x, rows_sampled: int, pattern=None):
     """The oracle as it stands, timed on this host on a sample of the workload:
     the full linear layer of one (b, h) head, and `rows_sampled` query rows of
     the softmax anchor of one head (rows are independent, each costs the same),
-    extrapolated to one whole group."""
+    extrapolated to one whole group.  With a block-sparse pattern the rows are
+    whole query blocks and the extrapolation is by query-key pairs."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -74,21 +84,46 @@ def cpu_baseline(w, x, rows_sampled: int):
     oracle.linear_attention(q, k, v, g)
     t_lin = time.perf_counter() - t0
     q, k, v, g = (to_f64(x[n][3, 0, 0]) for n in "QKVG")
-    rows = np.random.default_rng(0).choice(w.N, size=min(rows_sampled, w.N), replace=False)
-    t0 = time.perf_counter()
-    oracle.softmax_attention(q, k, v, g, rows=rows)
-    t_rows = time.perf_counter() - t0
+    if pattern is None:
+        rows = np.random.default_rng(0).choice(w.N, size=min(rows_sampled, w.N), replace=False)
+        t0 = time.perf_counter()
+        oracle.softmax_attention(q, k, v, g, rows=rows)
+        t_rows = time.perf_counter() - t0
+        scale = w.N / rows.size
+    else:
+        offsets, indices = pattern
+        nqb = len(offsets) - 1
+        qbs = np.linspace(0, nqb - 1, num=max(1, min(nqb, rows_sampled // 256))).astype(np.int64)
+        rows = np.concatenate([np.arange(qb * 256, min(w.N, (qb + 1) * 256)) for qb in np.unique(qbs)])
+        t0 = time.perf_counter()
+        oracle.softmax_attention_blocksparse(q, k, v, g, offsets, indices, rows=rows)
+        t_rows = time.perf_counter() - t0
+        pairs = pattern_pairs(w.N, offsets, indices)
+        sampled = sum(pattern_pairs(w.N, offsets, indices, only=int(qb)) for qb in np.unique(qbs))
+        scale = pairs / sampled
     heads = w.B * w.H
-    t_group = 3 * heads * t_lin + heads * (w.N / rows.size) * t_rows
+    t_group = 3 * heads * t_lin + heads * scale * t_rows
     return {
         "value": w.B * w.N / t_group,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"float64 numpy oracle: full linear layer of 1 of {heads} heads ({t_lin:.2f} s) and "
-                   f"{rows.size} of {w.N} softmax query rows of 1 head ({t_rows:.2f} s), extrapolated "
+                   f"{rows.size} of {w.N} {'block-sparse ' if pattern else ''}softmax query rows of 1 head "
+                   f"({t_rows:.2f} s), extrapolated "
                    f"to 3 linear + 1 softmax layers over {heads} heads ({t_group:.0f} s per group)"),
     }
+
+
+def pattern_pairs(N, offsets, indices, only=None):
+    """Query-key pairs a block pattern keeps (valid keys only, set semantics)."""
+    nkb = -(-N // 64)
+    total = 0
+    for qb in (range(len(offsets) - 1) if only is None else [only]):
+        rows = min(N, (qb + 1) * 256) - qb * 256
+        blocks = {int(b) for b in indices[offsets[qb]:offsets[qb + 1]] if 0 <= b < nkb}
+        total += rows * sum(min(64, N - 64 * b) for b in blocks)
+    return total
 
 
 def main():
@@ -101,6 +136,8 @@ def main():
                     help="steps of the all-softmax group (4 anchors) for the speedup ratio; 0 skips")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="softmax rows the oracle baseline samples")
+    ap.add_argument("--anchor", choices=("dense", "lvsa"), default="dense",
+                    help="dense softmax anchor (default) or the block-sparse LVSA anchor")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -118,6 +155,14 @@ def main():
     w = get(args.config)
     if w.dtype != "bf16":
         raise SystemExit("bench workloads are the bf16 shapes; the fp32 tiny shape is a test case")
+    sparse = args.anchor == "lvsa"
+    label = f"{w.name}_lvsa" if sparse else w.name
+    pattern = None
+    if sparse:
+        from workloads.sparsity import lvsa_pattern, pattern_density
+        pattern = lvsa_pattern(w.frames, w.grid[0] * w.grid[1])
+        print(f"[bench] LVSA pattern: {pattern[1].size} key blocks, density "
+              f"{pattern_density(pattern[0], w.N):.4f}", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}; generating inputs", file=sys.stderr,
@@ -137,9 +182,27 @@ def main():
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(max(args.steps, 1))]
 
-    def step(i=None):
-        ha.hybrid_attn_group(x["Q"], x["K"], x["V"], x["G"], O4, workspace=ws,
-                             events=None if i is None else evs[i])
+    if not sparse:
+        def step(i=None):
+            ha.hybrid_attn_group(x["Q"], x["K"], x["V"], x["G"], O4, workspace=ws,
+                                 events=None if i is None else evs[i])
+    else:
+        off_d = torch.from_numpy(pattern[0]).to(dev)
+        idx_d = torch.from_numpy(pattern[1]).to(dev)
+
+        def step(i=None):
+            # the same group with the anchor swapped for the block-sparse kernel;
+            # events are recorded on the stream the kernels run on
+            e = None if i is None else evs[i]
+            if e is not None:
+                e[0].record()
+            for l in range(3):
+                ha.hybrid_attn_linear(x["Q"][l], x["K"][l], x["V"][l], x["G"][l], O4[l], workspace=ws)
+                if e is not None:
+                    e[l + 1].record()
+            ha.hybrid_attn_softmax_blocksparse(x["Q"][3], x["K"][3], x["V"][3], x["G"][3], off_d, idx_d, O=O4[3])
+            if e is not None:
+                e[4].record()
 
     for _ in range(args.warmup):
         step()
@@ -161,16 +224,18 @@ def main():
 
     BH = w.B * w.H
     anchor_ms = layer_ms[3]
-    anchor_flop = 4.0 * BH * w.N * w.N * w.d          # QK^T and PV, 2 flops per multiply-add
+    pairs = pattern_pairs(w.N, *pattern) if sparse else w.N * w.N
+    anchor_flop = 4.0 * BH * pairs * w.d              # QK^T and PV, 2 flops per multiply-add
     achieved = anchor_flop / (anchor_ms / 1e3) / 1e12
     roofline = {
-        "kernel": "anchor_bf16 (gated softmax anchor)",
+        "kernel": ("anchor_bf16<SPARSE> (block-sparse gated softmax anchor)" if sparse
+                   else "anchor_bf16 (gated softmax anchor)"),
         "bound": "mfma",
         "achieved": round(achieved, 1),
         "peak": MFMA_BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-        "traffic": measured_traffic(w.name),
+        "traffic": measured_traffic(label),
     }
     lin_ms = sum(layer_ms[:3]) / 3
     lin_bytes = BH * w.N * w.d * 2 * 5                 # Q, K, V, G read + O written, bf16
@@ -179,7 +244,21 @@ def main():
         "linear_layer_hbm_gbs": round(lin_bytes / (lin_ms / 1e3) / 1e9, 1),
     }
 
-    if args.allsoftmax_steps > 0:
+    if sparse:
+        extra["pattern_density"] = round(pairs / (w.N * w.N), 5)
+        extra["anchor_pairs"] = pairs
+    if sparse and args.allsoftmax_steps > 0:
+        # one dense anchor on the same inputs: what the pattern saves
+        ha.hybrid_attn_softmax(x["Q"][3], x["K"][3], x["V"][3], x["G"][3], O4[3])
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        ha.hybrid_attn_softmax(x["Q"][3], x["K"][3], x["V"][3], x["G"][3], O4[3])
+        a1.record()
+        torch.cuda.synchronize()
+        extra["dense_anchor_ms"] = round(a0.elapsed_time(a1), 3)
+        extra["sparse_anchor_speedup_vs_dense"] = round(a0.elapsed_time(a1) / anchor_ms, 3)
+    elif args.allsoftmax_steps > 0:
         def soft4():
             for l in range(4):
                 ha.hybrid_attn_softmax(x["Q"][l], x["K"][l], x["V"][l], x["G"][l], O4[l])
@@ -199,10 +278,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x, args.cpu_rows)
+        cpu = cpu_baseline(w, x, args.cpu_rows, pattern)
 
     line = {
-        "metric": "hybrid 3:1 attention group tokens/s at 720p/5s shape; % of bf16 MFMA/HBM peak",
+        "metric": ("hybrid 3:1 attention group (block-sparse LVSA anchor) tokens/s; % of bf16 MFMA peak"
+                   if sparse else "hybrid 3:1 attention group tokens/s at 720p/5s shape; % of bf16 MFMA/HBM peak"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -215,7 +295,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "layers": "linear,linear,linear,softmax", "parallelism": "single-gpu"},
+                   "layers": "linear,linear,linear," + ("softmax_blocksparse_lvsa" if sparse else "softmax"),
+                   "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         **extra,

@@ -19,12 +19,16 @@ __all__ = [
     "hybrid_attn_kv_state",
     "hybrid_attn_linear",
     "hybrid_attn_softmax",
+    "hybrid_attn_softmax_blocksparse",
+    "SPARSE_BLOCK_Q",
+    "SPARSE_BLOCK_K",
     "hybrid_attn_group",
     "hybrid_attn_group_schedule",
     "LAYER_KINDS",
 ]
 
 LAYER_KINDS = {0: "linear", 1: "softmax"}
+SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 256, 64   # HA_SPARSE_BLOCK_Q / HA_SPARSE_BLOCK_K
 _DTYPES = {torch.bfloat16: HA_BF16, torch.float32: HA_F32}
 
 
@@ -118,6 +122,31 @@ def hybrid_attn_softmax(Q, K, V, G, O=None, stream=None):
     _check(_lib.load().hybrid_attn_softmax(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), B, H, N, d,
                                            _dtype_code(ref), _stream(stream)),
            "hybrid_attn_softmax")
+    return O
+
+
+def hybrid_attn_softmax_blocksparse(Q, K, V, G, block_offsets, block_indices, O=None, stream=None):
+    """Block-sparse gated softmax anchor; Q, K, V, G, O: [B, H, N, d].  The
+    pattern is CSR over query blocks of SPARSE_BLOCK_Q rows: int32 device
+    tensors block_offsets [ceil(N / SPARSE_BLOCK_Q) + 1] and block_indices
+    (key blocks of SPARSE_BLOCK_K keys, distinct within a query block)."""
+    ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
+    B, H, N, d = ref.shape
+    nqb = -(-N // SPARSE_BLOCK_Q)
+    for n, t in (("block_offsets", block_offsets), ("block_indices", block_indices)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1:
+            raise ValueError(f"{n} must be a 1-d int32 tensor")
+        if not t.is_contiguous() or t.device != ref.device:
+            raise ValueError(f"{n} must be contiguous on {ref.device}")
+    if block_offsets.numel() != nqb + 1:
+        raise ValueError(f"block_offsets: {nqb + 1} entries expected for N={N}, got {block_offsets.numel()}")
+    O = torch.empty_like(ref) if O is None else O
+    n_idx = block_indices.numel()
+    idx_ptr = _ptr(block_indices) if n_idx > 0 else ctypes.c_void_p(None)
+    _check(_lib.load().hybrid_attn_softmax_blocksparse(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), B, H, N,
+                                                       d, _dtype_code(ref), _ptr(block_offsets), idx_ptr,
+                                                       n_idx, _stream(stream)),
+           "hybrid_attn_softmax_blocksparse")
     return O
 
 

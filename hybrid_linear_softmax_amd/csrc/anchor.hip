@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kBr = 256;  // queries per block (8 waves x 32)
 constexpr int kBc = 64;   // keys per iteration
+static_assert(kBr == kSparseBlockQ && kBc == kSparseBlockK, "sparse pattern blocks are the tile sizes");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest unrescaled probability
 
@@ -52,13 +53,20 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 
-template <int D>
+// SPARSE: the query block walks the key blocks listed for it in a CSR pattern
+// (blk_off / blk_idx) instead of all key blocks.  Listed indices outside
+// [0, ceil(N/64)) are read as empty blocks (buffer loads past the head read
+// zeros and every key is masked); offsets are clamped to [0, n_idx].
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__ Q,
                                                       const bf16_t* __restrict__ K,
                                                       const bf16_t* __restrict__ V,
                                                       const bf16_t* __restrict__ G,
                                                       bf16_t* __restrict__ O, int64_t N,
-                                                      int64_t qblocks, int64_t total, float c) {
+                                                      int64_t qblocks, int64_t total, float c,
+                                                      const int32_t* __restrict__ blk_off,
+                                                      const int32_t* __restrict__ blk_idx,
+                                                      int64_t n_idx) {
   constexpr int NT = 512;
   constexpr int KP = D + 8;              // LDS pitch of K rows (elements)
   constexpr int VP = kBc + 8;            // LDS pitch of V^T rows (elements)
@@ -85,6 +93,24 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
       __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, (int)head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rV =
       __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, (int)head_bytes, 0x00020000);
+
+  // key blocks of this query block: dense 0 .. nkb-1, or the CSR list
+  const int64_t nkb = (N + kBc - 1) / kBc;
+  int64_t list_beg = 0, nsteps = nkb;
+  if (SPARSE) {
+    const int64_t qb = id % qblocks;
+    list_beg = min(max((int64_t)blk_off[qb], (int64_t)0), n_idx);
+    const int64_t list_end = min(max((int64_t)blk_off[qb + 1], list_beg), n_idx);
+    nsteps = list_end - list_beg;
+  }
+  // first key of step i (a past-the-end offset, whose loads read zeros, for an
+  // invalid or absent block) and the number of valid keys of that block
+  auto block_key0 = [&](int64_t i) -> int64_t {
+    if (!SPARSE) return i * kBc;
+    const int64_t b = i < nsteps ? (int64_t)blk_idx[list_beg + i] : -1;
+    return (b >= 0 && b < nkb) ? b * kBc : nkb * kBc;
+  };
+  auto block_valid = [&](int64_t k0) -> int { return static_cast<int>(min((int64_t)kBc, max((int64_t)0, N - k0))); };
 
   bf16x8 qf[KS];
 #pragma unroll
@@ -123,8 +149,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
       }
     }
   };
-  auto mask = [&](f32x16 (&s)[2], int64_t k0) {
-    const int lim = static_cast<int>(max((int64_t)0, N - k0));
+  auto mask = [&](f32x16 (&s)[2], int lim) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -153,7 +178,8 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   };
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   auto softmax_p = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2]) {
-    const float mc = m * c;
+    // (sparse) while every key seen so far was masked, m = -inf: keep p = 0
+    const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -221,10 +247,10 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     }
   };
   // prologue: K_0, V_0 -> buffers 0, K_1 -> K buffer 1; S_0
-  load_k(0);
-  load_v(0);
+  load_k(block_key0(0));
+  load_v(block_key0(0));
   store_kv(0, 0);
-  load_k(kBc);
+  load_k(block_key0(1));
 #pragma unroll
   for (int i = 0; i < KCH; ++i) {
     const int cidx = tid + NT * i;
@@ -233,16 +259,22 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   __syncthreads();
   f32x16 sa[2], sb[2];
   qk(0, sa);
-  if (kBc > N) mask(sa, 0);
+  {
+    const int lim = block_valid(block_key0(0));
+    if (lim < kBc) mask(sa, lim);
+  }
   m = rowmax(sa);
   __syncthreads();
   auto step = [&](int64_t j, f32x16 (&scur)[2], f32x16 (&snext)[2], auto masked) {
-    load_k((j + 2) * kBc);
+    load_k(block_key0(j + 2));
     bf16x8 pf[2][2];
     qk(static_cast<int>((j + 1) & 1), snext);
     softmax_p(scur, pf);
-    load_v((j + 1) * kBc);  // V is stored at the end of the step: short live range
-    if (decltype(masked)::value) mask(snext, (j + 1) * kBc);
+    load_v(block_key0(j + 1));  // V is stored at the end of the step: short live range
+    if (SPARSE || decltype(masked)::value) {
+      const int lim = block_valid(block_key0(j + 1));
+      if (lim < kBc) mask(snext, lim);
+    }
     pv(static_cast<int>(j & 1), pf);
     const float mx = rowmax(snext);
     store_kv(static_cast<int>(j & 1), static_cast<int>((j + 1) & 1));
@@ -251,20 +283,22 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;
-  const int64_t nkb = (N + kBc - 1) / kBc;
-  const int64_t nfull = N / kBc;  // blocks 0 .. nfull-1 hold 64 valid keys
+  // dense: blocks 0 .. nfull-1 hold 64 valid keys, so only the last steps mask;
+  // sparse: every step checks the next listed block at run time
+  const int64_t nfull = SPARSE ? 0 : N / kBc;
   int64_t j = 0;
   for (; j + 2 < nfull; j += 2) {
     step(j, sa, sb, NoMask{});
     step(j + 1, sb, sa, NoMask{});
   }
-  for (; j < nkb; j += 2) {
+  for (; j < nsteps; j += 2) {
     step(j, sa, sb, Mask{});
-    if (j + 1 < nkb) step(j + 1, sb, sa, Mask{});
+    if (j + 1 < nsteps) step(j + 1, sb, sa, Mask{});
   }
 
   const float l = lsum + __shfl_xor(lsum, 32);
-  const float inv = __builtin_amdgcn_rcpf(l);
+  // (sparse) a query block with no valid key has l = 0 and gets O = 0
+  const float inv = (SPARSE && !(l > 0.f)) ? 0.f : __builtin_amdgcn_rcpf(l);
   if (qrow < N) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -284,14 +318,18 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
 }
 
 // Plain float32 anchor: two lanes per query (each half of d), 64 queries per
-// block, 32-key blocks in LDS, online softmax per key block.
-template <int D>
+// block, 32-key blocks in LDS, online softmax per key block.  SPARSE walks the
+// 64-key blocks listed for the enclosing 256-query block, as two 32-key halves.
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
                                                   const float* __restrict__ K,
                                                   const float* __restrict__ V,
                                                   const float* __restrict__ G,
                                                   float* __restrict__ O, int64_t N,
-                                                  int64_t qblocks, float scale) {
+                                                  int64_t qblocks, float scale,
+                                                  const int32_t* __restrict__ blk_off,
+                                                  const int32_t* __restrict__ blk_idx,
+                                                  int64_t n_idx) {
   constexpr int BQ = 64, BK = 32, HD = D / 2;
   __shared__ float sK[BK][D];
   __shared__ float sV[BK][D];
@@ -307,7 +345,21 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  for (int64_t k0 = 0; k0 < N; k0 += BK) {
+  const int64_t nkb = (N + kBc - 1) / kBc;
+  int64_t list_beg = 0, nsteps = (N + BK - 1) / BK;
+  if (SPARSE) {
+    const int64_t qb = (blockIdx.x % qblocks) * BQ / kBr;
+    list_beg = min(max((int64_t)blk_off[qb], (int64_t)0), n_idx);
+    const int64_t list_end = min(max((int64_t)blk_off[qb + 1], list_beg), n_idx);
+    nsteps = (list_end - list_beg) * (kBc / BK);
+  }
+  for (int64_t i = 0; i < nsteps; ++i) {
+    int64_t k0 = i * BK;
+    if (SPARSE) {
+      const int64_t b = blk_idx[list_beg + i / (kBc / BK)];
+      if (b < 0 || b >= nkb) continue;  // the same for every thread of the block
+      k0 = b * kBc + (i % (kBc / BK)) * BK;
+    }
     __syncthreads();
     for (int e = tid; e < BK * D; e += 128) {
       const int64_t key = k0 + e / D;
@@ -327,6 +379,7 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
       mx = fmaxf(mx, sc[j]);
     }
     const float m_new = fmaxf(m, mx);
+    if (m_new == -INFINITY) continue;  // no valid key yet (sparse tail halves)
     const float alpha = expf(m - m_new);
     l *= alpha;
 #pragma unroll
@@ -344,7 +397,7 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
 #pragma unroll
     for (int e = 0; e < HD; ++e) {
       const int64_t off = base + qrow * D + half * HD + e;
-      O[off] = gate_exact(G[off]) * (acc[e] / l);
+      O[off] = l > 0.f ? gate_exact(G[off]) * (acc[e] / l) : 0.f;
     }
   }
 }
@@ -352,8 +405,10 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
 }  // namespace
 
 hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const void* V,
-                         const void* G, void* O, int64_t BH, int64_t N, hipStream_t s) {
+                         const void* G, void* O, int64_t BH, int64_t N, hipStream_t s,
+                         const int32_t* blk_off, const int32_t* blk_idx, int64_t n_idx) {
   if (BH == 0 || N == 0) return hipSuccess;
+  const bool sparse = blk_off != nullptr;
   if (bf16) {
     const int64_t qb = (N + kBr - 1) / kBr;
     const int64_t total = BH * qb;
@@ -364,10 +419,11 @@ hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const v
     const bf16_t* g = static_cast<const bf16_t*>(G);
     bf16_t* o = static_cast<bf16_t*>(O);
     const dim3 grid(static_cast<unsigned>(total)), block(512);
+    auto go = [&](auto kern) { kern<<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, total, c, blk_off, blk_idx, n_idx); };
     if (d == 128)
-      anchor_bf16<128><<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, total, c);
+      sparse ? go(anchor_bf16<128, true>) : go(anchor_bf16<128, false>);
     else
-      anchor_bf16<64><<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, total, c);
+      sparse ? go(anchor_bf16<64, true>) : go(anchor_bf16<64, false>);
   } else {
     const int64_t qb = (N + 63) / 64;
     const float scale = 1.0f / sqrtf(static_cast<float>(d));
@@ -377,10 +433,11 @@ hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const v
     const float* g = static_cast<const float*>(G);
     float* o = static_cast<float*>(O);
     const dim3 grid(static_cast<unsigned>(BH * qb)), block(128);
+    auto go = [&](auto kern) { kern<<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, scale, blk_off, blk_idx, n_idx); };
     if (d == 128)
-      anchor_f32<128><<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, scale);
+      sparse ? go(anchor_f32<128, true>) : go(anchor_f32<128, false>);
     else
-      anchor_f32<64><<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, scale);
+      sparse ? go(anchor_f32<64, true>) : go(anchor_f32<64, false>);
   }
   return hipGetLastError();
 }

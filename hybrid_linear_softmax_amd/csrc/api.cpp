@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <climits>
+
 #include <hip/hip_runtime_api.h>
 
 #include "../../include/hybrid_attn.h"
@@ -189,6 +191,31 @@ HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, cons
   st = check_buffers(in, 4, p.tensor_bytes, O, p.tensor_bytes);
   if (st != HA_OK) return st;
   return hip_status(ha::launch_anchor(p.bf16, d, Q, K, V, G, O, p.BH, p.N, stream));
+}
+
+HA_API int hybrid_attn_softmax_blocksparse(const void* Q, const void* K, const void* V, const void* G,
+                                           void* O, int B, int H, int64_t N, int d, ha_dtype dtype,
+                                           const int32_t* block_offsets, const int32_t* block_indices,
+                                           int64_t num_indices, hipStream_t stream) {
+  static_assert(HA_SPARSE_BLOCK_Q == ha::kSparseBlockQ && HA_SPARSE_BLOCK_K == ha::kSparseBlockK,
+                "pattern block sizes");
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const void* in[4] = {Q, K, V, G};
+  st = check_buffers(in, 4, p.tensor_bytes, O, p.tensor_bytes);
+  if (st != HA_OK) return st;
+  if (block_offsets == nullptr || num_indices < 0 || num_indices > INT32_MAX) return HA_EINVAL;
+  if (block_indices == nullptr && num_indices > 0) return HA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(block_offsets) & 3u) || (reinterpret_cast<uintptr_t>(block_indices) & 3u))
+    return HA_EALIGN;
+  const size_t off_bytes = static_cast<size_t>((p.N + HA_SPARSE_BLOCK_Q - 1) / HA_SPARSE_BLOCK_Q + 1) * 4u;
+  if (overlaps(block_offsets, off_bytes, O, p.tensor_bytes) ||
+      (num_indices > 0 && overlaps(block_indices, static_cast<size_t>(num_indices) * 4u, O, p.tensor_bytes)))
+    return HA_EINVAL;
+  return hip_status(ha::launch_anchor(p.bf16, d, Q, K, V, G, O, p.BH, p.N, stream, block_offsets,
+                                      block_indices, num_indices));
 }
 
 HA_API int hybrid_attn_group_timed(const void* Q4, const void* K4, const void* V4, const void* G4,

@@ -39,8 +39,15 @@ hipError_t launch_kv_reduce(bool bf16, int d, const float* part, float* S, float
 hipError_t launch_apply(bool bf16, int d, const void* Q, const void* G, void* O, const float* S,
                         const float* z, const uint16_t* St_hi, const uint16_t* St_lo, int64_t BH,
                         int64_t N, float eps, hipStream_t s);
-// R3: gated softmax anchor (flash-style, online softmax).
+// Query / key block sizes of the block-sparse anchor's pattern.
+constexpr int kSparseBlockQ = 256;
+constexpr int kSparseBlockK = 64;
+// R3: gated softmax anchor (flash-style, online softmax).  With blk_off set,
+// block-sparse: query block qb (kSparseBlockQ rows) attends to the key blocks
+// (kSparseBlockK keys) blk_idx[blk_off[qb] .. blk_off[qb+1]-1], n_idx entries.
 hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const void* V,
-                         const void* G, void* O, int64_t BH, int64_t N, hipStream_t s);
+                         const void* G, void* O, int64_t BH, int64_t N, hipStream_t s,
+                         const int32_t* blk_off = nullptr, const int32_t* blk_idx = nullptr,
+                         int64_t n_idx = 0);
 
 }  // namespace ha

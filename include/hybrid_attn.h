@@ -102,6 +102,37 @@ HA_API int hybrid_attn_linear(const void* Q, const void* K, const void* V, const
 HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, const void* G, void* O,
                                int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream);
 
+/* Block sizes of the block-sparse anchor's pattern: query block qb holds rows
+ * qb*256 .. qb*256+255 and key block kb holds keys kb*64 .. kb*64+63 of each
+ * (b, h); the last blocks of a sequence may be partial. */
+#define HA_SPARSE_BLOCK_Q 256
+#define HA_SPARSE_BLOCK_K 64
+
+/* Block-sparse gated softmax anchor: the anchor above with each query attending
+ * only to the keys of the key blocks its query block lists, i.e. the softmax is
+ * taken over the union of those blocks' keys.  This is the block-sparse
+ * attention of the pages' long-video setting (LongVie Sparse Attention: the
+ * review page, section 3, and the summary page, section 03, where the anchor
+ * of the 60-second model attends to a window of frames plus periodic global
+ * frames).  The pattern, shared by every batch item and head, is in CSR form in
+ * device memory:
+ *   block_offsets: int32 [ceil(N / HA_SPARSE_BLOCK_Q) + 1], non-decreasing,
+ *                  block_offsets[0] = 0, last entry = num_indices;
+ *   block_indices: int32 [num_indices]; query block qb lists the key blocks
+ *                  block_indices[block_offsets[qb] .. block_offsets[qb+1]-1].
+ * Indices must be distinct within a query block (any order); an index outside
+ * [0, ceil(N / HA_SPARSE_BLOCK_K)) names no key and is ignored; offsets are
+ * clamped to [0, num_indices].  A query block with no valid key writes O = 0.
+ * The pattern is read, never written; it must not overlap O.  HA_EINVAL for a
+ * NULL block_offsets, a NULL block_indices with num_indices > 0, or
+ * num_indices outside [0, 2^31 - 1]; HA_EALIGN for pattern arrays that are not
+ * 4-byte aligned.  The full pattern (every key block for every query block)
+ * gives the dense anchor's result. */
+HA_API int hybrid_attn_softmax_blocksparse(const void* Q, const void* K, const void* V, const void* G,
+                                           void* O, int B, int H, int64_t N, int d, ha_dtype dtype,
+                                           const int32_t* block_offsets, const int32_t* block_indices,
+                                           int64_t num_indices, hipStream_t stream);
+
 /* One hybrid group: layers 0, 1, 2 gated linear, layer 3 the gated softmax
  * anchor (the 3:1 ratio of the pages, anchor last in the period).  Q4, K4, V4,
  * G4 in and O4 out are stacked [4, B, H, N, d] arrays; layer l of the output is

@@ -12,7 +12,7 @@ OK, EINVAL, EUNSUP, EALIGN, EWS = _lib.HA_OK, _lib.HA_EINVAL, _lib.HA_EUNSUPPORT
 
 # Fake, distinct, 256-byte aligned "device" addresses: validation only compares them.
 GB = 1 << 30
-Q, K, V, G, O, WS, S, Z = (GB * (i + 1) for i in range(8))
+Q, K, V, G, O, WS, S, Z, OFF, IDX = (GB * (i + 1) for i in range(10))
 
 
 @pytest.fixture(scope="module")
@@ -63,7 +63,11 @@ def _softmax(lib, q=Q, k=K, v=V, g=G, o=O, B=1, H=2, N=100, d=64, dt=HA_BF16):
     return lib.hybrid_attn_softmax(q, k, v, g, o, B, H, N, d, dt, None)
 
 
-@pytest.mark.parametrize("call", [_linear, _softmax])
+def _softmax_bs(lib, q=Q, k=K, v=V, g=G, o=O, B=1, H=2, N=100, d=64, dt=HA_BF16, off=OFF, idx=IDX, n=7):
+    return lib.hybrid_attn_softmax_blocksparse(q, k, v, g, o, B, H, N, d, dt, off, idx, n, None)
+
+
+@pytest.mark.parametrize("call", [_linear, _softmax, _softmax_bs])
 def test_argument_errors(lib, call):
     assert call(lib, d=96) == EUNSUP
     assert call(lib, d=0) == EUNSUP
@@ -94,6 +98,21 @@ def test_workspace_errors(lib):
     assert lib.hybrid_attn_kv_state(K, V, None, Z, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
     assert lib.hybrid_attn_kv_state(K, V, S, S + 64, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
     assert lib.hybrid_attn_kv_state(K, V, K, Z, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
+
+
+def test_blocksparse_pattern_errors(lib):
+    # (only rejected calls here: a valid one would launch on the fake addresses)
+    assert _softmax_bs(lib, off=None) == EINVAL
+    assert _softmax_bs(lib, idx=None) == EINVAL
+    assert _softmax_bs(lib, n=-1) == EINVAL
+    assert _softmax_bs(lib, n=1 << 31) == EINVAL
+    assert _softmax_bs(lib, off=OFF + 2) == EALIGN
+    assert _softmax_bs(lib, idx=IDX + 1) == EALIGN
+    assert _softmax_bs(lib, off=O + 64) == EINVAL         # the output may not overwrite the pattern
+    assert _softmax_bs(lib, idx=O - 8, n=4) == EINVAL
+    # the size checks run first: a bad head dimension wins over a bad pattern
+    assert _softmax_bs(lib, d=96, off=None) == EUNSUP
+    assert lib.hybrid_attn_softmax_blocksparse(Q, K, V, G, O, 1, 2, 0, 64, HA_BF16, None, None, 0, None) == OK
 
 
 def test_group_errors(lib):

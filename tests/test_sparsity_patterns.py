@@ -40,3 +40,21 @@ def test_block_pattern_covers_frames():
 def test_full_budget_is_dense():
     off, idx = lvsa_pattern(6, 64, C=6)
     assert pattern_density(off, 6 * 64) == 1.0
+
+
+def test_random_and_full_patterns():
+    from workloads.sparsity import full_pattern, random_pattern
+    N = 3000
+    nqb, nkb = -(-N // 256), -(-N // 64)
+    off, idx = full_pattern(N)
+    assert off.dtype == np.int32 and idx.dtype == np.int32 and len(off) == nqb + 1
+    assert all(list(idx[off[q]:off[q + 1]]) == list(range(nkb)) for q in range(nqb))
+    base = random_pattern(N, keep=0.4, seed=3, empty_every=4)
+    mixed = random_pattern(N, keep=0.4, seed=3, empty_every=4, invalid=3, shuffle=True)
+    for q in range(nqb):
+        a = base[1][base[0][q]:base[0][q + 1]]
+        b = mixed[1][mixed[0][q]:mixed[0][q + 1]]
+        assert len(set(a)) == len(a) and len(set(b)) == len(b)          # distinct
+        assert set(a) == {x for x in b if 0 <= x < nkb}                 # same valid set
+        assert len(b) == len(a) + 3
+        assert (len(a) == 0) == (q % 4 == 0)

@@ -77,3 +77,39 @@ def pattern_density(offsets, N: int, block_q: int = SPARSE_BLOCK_Q, block_k: int
     nqb = len(offsets) - 1
     nkb = -(-N // block_k)
     return float(np.diff(offsets).sum()) / (nqb * nkb)
+
+
+def full_pattern(N: int, block_q: int = SPARSE_BLOCK_Q, block_k: int = SPARSE_BLOCK_K):
+    """Every key block for every query block (the dense anchor as a pattern)."""
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    offsets = np.arange(nqb + 1, dtype=np.int64) * nkb
+    indices = np.tile(np.arange(nkb, dtype=np.int32), nqb)
+    return offsets.astype(np.int32), indices
+
+
+def random_pattern(N: int, keep: float = 0.3, seed: int = 0, empty_every: int = 0,
+                   invalid: int = 0, shuffle: bool = False,
+                   block_q: int = SPARSE_BLOCK_Q, block_k: int = SPARSE_BLOCK_K):
+    """Seeded unstructured pattern: each query block keeps a random subset of
+    about keep * nkb distinct key blocks (at least one).  empty_every > 0 leaves
+    every empty_every-th query block with no block; invalid > 0 appends that many
+    out-of-range indices (-1, nkb, nkb + 7, ...) to every list; shuffle puts each
+    list in random order.  Indices stay distinct within a query block."""
+    rng = np.random.default_rng(seed)
+    order_rng = np.random.default_rng([seed, 1])   # the order never changes the sets
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    bad = [-1, nkb, nkb + 7, -1000, 2 * nkb + 3][:invalid]
+    offsets = [0]
+    indices = []
+    for qb in range(nqb):
+        if empty_every and qb % empty_every == 0:
+            blocks = []
+        else:
+            n = min(nkb, max(1, int(round(keep * nkb))))
+            blocks = sorted(rng.choice(nkb, size=n, replace=False).tolist())
+        blocks = blocks + bad
+        if shuffle:
+            order_rng.shuffle(blocks)
+        indices.extend(blocks)
+        offsets.append(len(indices))
+    return np.asarray(offsets, dtype=np.int32), np.asarray(indices, dtype=np.int32)
