@@ -103,12 +103,21 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     const int64_t list_end = min(max((int64_t)blk_off[qb + 1], list_beg), n_idx);
     nsteps = list_end - list_beg;
   }
-  // first key of step i (a past-the-end offset, whose loads read zeros, for an
-  // invalid or absent block) and the number of valid keys of that block
-  auto block_key0 = [&](int64_t i) -> int64_t {
+  // (sparse) list entries are fetched with vector buffer loads two steps before
+  // their use, so the wait for them is covered by the K/V loads in between;
+  // loads past the list read 0 and are discarded by the i < nsteps test
+  const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(SPARSE ? blk_idx + list_beg : blk_off), (short)0,
+      SPARSE ? (int)(nsteps * 4) : 0, 0x00020000);
+  auto fetch_entry = [&](int64_t i) -> int32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(rL, (int)(min(i, nsteps) * 4), 0, 0);
+  };
+  // first key of step i's block; an absent or out-of-range block maps to a
+  // past-the-end offset, whose loads read zeros and whose keys are all masked
+  auto key0_of = [&](int64_t i, int32_t entry) -> int64_t {
     if (!SPARSE) return i * kBc;
-    const int64_t b = i < nsteps ? (int64_t)blk_idx[list_beg + i] : -1;
-    return (b >= 0 && b < nkb) ? b * kBc : nkb * kBc;
+    const int32_t e = __builtin_amdgcn_readfirstlane(entry);
+    return (i < nsteps && e >= 0 && e < nkb) ? (int64_t)e * kBc : nkb * kBc;
   };
   auto block_valid = [&](int64_t k0) -> int { return static_cast<int>(min((int64_t)kBc, max((int64_t)0, N - k0))); };
 
@@ -247,10 +256,20 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     }
   };
   // prologue: K_0, V_0 -> buffers 0, K_1 -> K buffer 1; S_0
-  load_k(block_key0(0));
-  load_v(block_key0(0));
+  int32_t e1 = 0, e2 = 0;  // (sparse) list entries of steps j+1 and j+2
+  if (SPARSE) {
+    const int32_t e0 = fetch_entry(0);
+    e1 = fetch_entry(1);
+    e2 = fetch_entry(2);
+    const int64_t k0 = key0_of(0, e0);
+    load_k(k0);
+    load_v(k0);
+  } else {
+    load_k(0);
+    load_v(0);
+  }
   store_kv(0, 0);
-  load_k(block_key0(1));
+  load_k(key0_of(1, e1));
 #pragma unroll
   for (int i = 0; i < KCH; ++i) {
     const int cidx = tid + NT * i;
@@ -260,22 +279,25 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   f32x16 sa[2], sb[2];
   qk(0, sa);
   {
-    const int lim = block_valid(block_key0(0));
+    const int lim = SPARSE ? block_valid(key0_of(0, fetch_entry(0))) : static_cast<int>(min((int64_t)kBc, N));
     if (lim < kBc) mask(sa, lim);
   }
   m = rowmax(sa);
   __syncthreads();
-  auto step = [&](int64_t j, f32x16 (&scur)[2], f32x16 (&snext)[2], auto masked) {
-    load_k(block_key0(j + 2));
+  // step j: k1, k2 are the first keys of blocks j+1 and j+2; masked steps
+  // apply the key limit lim1 of block j+1 (in sparse mode only when it is
+  // below 64: the branch sits after the PV MFMAs, off the softmax-PV chain)
+  auto step = [&](int64_t j, int64_t k1, int64_t k2, int lim1, f32x16 (&scur)[2], f32x16 (&snext)[2],
+                  auto masked) {
+    load_k(k2);
     bf16x8 pf[2][2];
     qk(static_cast<int>((j + 1) & 1), snext);
     softmax_p(scur, pf);
-    load_v(block_key0(j + 1));  // V is stored at the end of the step: short live range
-    if (SPARSE || decltype(masked)::value) {
-      const int lim = block_valid(block_key0(j + 1));
-      if (lim < kBc) mask(snext, lim);
-    }
+    load_v(k1);  // V is stored at the end of the step: short live range
     pv(static_cast<int>(j & 1), pf);
+    if (decltype(masked)::value) {
+      if (!SPARSE || lim1 < kBc) mask(snext, lim1);
+    }
     const float mx = rowmax(snext);
     store_kv(static_cast<int>(j & 1), static_cast<int>((j + 1) & 1));
     rescale(mx);
@@ -283,17 +305,30 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;
-  // dense: blocks 0 .. nfull-1 hold 64 valid keys, so only the last steps mask;
-  // sparse: every step checks the next listed block at run time
-  const int64_t nfull = SPARSE ? 0 : N / kBc;
   int64_t j = 0;
-  for (; j + 2 < nfull; j += 2) {
-    step(j, sa, sb, NoMask{});
-    step(j + 1, sb, sa, NoMask{});
-  }
-  for (; j < nsteps; j += 2) {
-    step(j, sa, sb, Mask{});
-    if (j + 1 < nsteps) step(j + 1, sb, sa, Mask{});
+  if (!SPARSE) {
+    // blocks 0 .. nfull-1 hold 64 valid keys: only the last steps mask
+    const int64_t nfull = N / kBc;
+    for (; j + 2 < nfull; j += 2) {
+      step(j, (j + 1) * kBc, (j + 2) * kBc, kBc, sa, sb, NoMask{});
+      step(j + 1, (j + 2) * kBc, (j + 3) * kBc, kBc, sb, sa, NoMask{});
+    }
+    for (; j < nsteps; j += 2) {
+      step(j, (j + 1) * kBc, (j + 2) * kBc, block_valid((j + 1) * kBc), sa, sb, Mask{});
+      if (j + 1 < nsteps) step(j + 1, (j + 2) * kBc, (j + 3) * kBc, block_valid((j + 2) * kBc), sb, sa, Mask{});
+    }
+  } else {
+    auto sparse_step = [&](int64_t jj, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+      const int64_t k1 = key0_of(jj + 1, e1);
+      const int64_t k2 = key0_of(jj + 2, e2);
+      e1 = e2;
+      e2 = fetch_entry(jj + 3);
+      step(jj, k1, k2, block_valid(k1), scur, snext, Mask{});
+    };
+    for (; j < nsteps; j += 2) {
+      sparse_step(j, sa, sb);
+      if (j + 1 < nsteps) sparse_step(j + 1, sb, sa);
+    }
   }
 
   const float l = lsum + __shfl_xor(lsum, 32);

@@ -3,8 +3,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <climits>
-
 #include <hip/hip_runtime_api.h>
 
 #include "../../include/hybrid_attn.h"
@@ -206,7 +204,8 @@ HA_API int hybrid_attn_softmax_blocksparse(const void* Q, const void* K, const v
   const void* in[4] = {Q, K, V, G};
   st = check_buffers(in, 4, p.tensor_bytes, O, p.tensor_bytes);
   if (st != HA_OK) return st;
-  if (block_offsets == nullptr || num_indices < 0 || num_indices > INT32_MAX) return HA_EINVAL;
+  // list positions are 32-bit byte offsets inside the kernel: fewer than 2^30 entries
+  if (block_offsets == nullptr || num_indices < 0 || num_indices >= (int64_t{1} << 30)) return HA_EINVAL;
   if (block_indices == nullptr && num_indices > 0) return HA_EINVAL;
   if ((reinterpret_cast<uintptr_t>(block_offsets) & 3u) || (reinterpret_cast<uintptr_t>(block_indices) & 3u))
     return HA_EALIGN;

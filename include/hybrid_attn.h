@@ -125,7 +125,7 @@ HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, cons
  * clamped to [0, num_indices].  A query block with no valid key writes O = 0.
  * The pattern is read, never written; it must not overlap O.  HA_EINVAL for a
  * NULL block_offsets, a NULL block_indices with num_indices > 0, or
- * num_indices outside [0, 2^31 - 1]; HA_EALIGN for pattern arrays that are not
+ * num_indices outside [0, 2^30); HA_EALIGN for pattern arrays that are not
  * 4-byte aligned.  The full pattern (every key block for every query block)
  * gives the dense anchor's result. */
 HA_API int hybrid_attn_softmax_blocksparse(const void* Q, const void* K, const void* V, const void* G,

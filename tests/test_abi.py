@@ -106,6 +106,7 @@ def test_blocksparse_pattern_errors(lib):
     assert _softmax_bs(lib, idx=None) == EINVAL
     assert _softmax_bs(lib, n=-1) == EINVAL
     assert _softmax_bs(lib, n=1 << 31) == EINVAL
+    assert _softmax_bs(lib, n=1 << 30) == EINVAL
     assert _softmax_bs(lib, off=OFF + 2) == EALIGN
     assert _softmax_bs(lib, idx=IDX + 1) == EALIGN
     assert _softmax_bs(lib, off=O + 64) == EINVAL         # the output may not overwrite the pattern
