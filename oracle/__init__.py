@@ -1,5 +1,5 @@
 """Plain, slow CPU oracle (float64 numpy) for the Hybrid Linear-Softmax
-Attention group.  Test infrastructure only: the test suite, the smoke check and
+Attention group and the attention block around it.  Test infrastructure only: the test suite, the smoke check and
 the bench's CPU-baseline leg use it; the library path never does."""
 from .hybrid_ref import (  # noqa: F401
     EPS,
@@ -17,3 +17,4 @@ from .hybrid_ref import (  # noqa: F401
     layer,
     group,
 )
+from .block_ref import block, merge_heads, project_in, project_out, split_heads  # noqa: F401

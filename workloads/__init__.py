@@ -8,6 +8,8 @@ from .generate import (  # noqa: F401
     layer_inputs_host,
     layer_inputs_device,
     group_inputs_device,
+    block_inputs_host,
+    block_inputs_device,
     heavy_token_positions,
     to_f64,
 )

@@ -25,7 +25,7 @@ import torch
 from .configs import Workload
 
 TENSORS = ("Q", "K", "V", "G")
-_TID = {"Q": 0, "K": 1, "V": 2, "G": 3, "heavy": 4}
+_TID = {"Q": 0, "K": 1, "V": 2, "G": 3, "heavy": 4, "x": 5, "W_in": 6, "W_out": 7}
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -116,6 +116,56 @@ def group_inputs_device(w: Workload, device="cuda", layers: int = 4) -> dict:
     for layer in range(layers):
         layer_inputs_device(w, layer, device, out={n: stacked[n][layer] for n in TENSORS})
     return stacked
+
+
+# ---------------------------------------------------------------------------
+# Attention block: residual stream x [B, N, C] ~ N(0, 1) and, per sub-layer l,
+# W_in[l] [4C, C] and W_out[l] [C, C] ~ N(0, 1/C) (fan-in scaling, so that the
+# projected Q, K, V, G are about N(0, 1)), C = H * d.  One stream per (layer,
+# tensor) on the host; per (layer, tensor, slab) on the device.
+
+def block_inputs_host(w: Workload, *, B=None, H=None, N=None, d=None, layers: int = 4,
+                      device="cpu", out_scale: float = 1.0) -> dict:
+    """x [B, N, C], W_in [layers, 4C, C], W_out [layers, C, C] drawn on the host.
+    out_scale multiplies W_out (tests use it to give the update the size of x)."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    d = w.d if d is None else d
+    C = H * d
+    dt = torch_dtype(w)
+    rng = np.random.Generator(np.random.PCG64(_seed_seq(w, 0, "x")))
+    x = rng.standard_normal((B, N, C), dtype=np.float32)
+    W_in = np.empty((layers, 4 * C, C), dtype=np.float32)
+    W_out = np.empty((layers, C, C), dtype=np.float32)
+    for l in range(layers):
+        W_in[l] = np.random.Generator(np.random.PCG64(_seed_seq(w, l, "W_in"))).standard_normal(
+            (4 * C, C), dtype=np.float32) * np.float32(1.0 / math.sqrt(C))
+        W_out[l] = np.random.Generator(np.random.PCG64(_seed_seq(w, l, "W_out"))).standard_normal(
+            (C, C), dtype=np.float32) * np.float32(out_scale / math.sqrt(C))
+    return {"x": torch.from_numpy(x).to(dt).to(device),
+            "W_in": torch.from_numpy(W_in).to(dt).to(device),
+            "W_out": torch.from_numpy(W_out).to(dt).to(device)}
+
+
+def block_inputs_device(w: Workload, device="cuda", layers: int = 4) -> dict:
+    """The block inputs at the workload's full size, drawn on the GPU (x one
+    batch item at a time, each weight matrix as one slab)."""
+    C = w.H * w.d
+    dt = torch_dtype(w)
+    gen = torch.Generator(device=device)
+    x = torch.empty((w.B, w.N, C), dtype=dt, device=device)
+    for b in range(w.B):
+        gen.manual_seed(_torch_seed(w, 0, "x", b))
+        x[b].copy_(torch.randn((w.N, C), generator=gen, device=device, dtype=torch.float32))
+    W_in = torch.empty((layers, 4 * C, C), dtype=dt, device=device)
+    W_out = torch.empty((layers, C, C), dtype=dt, device=device)
+    for l in range(layers):
+        gen.manual_seed(_torch_seed(w, l, "W_in"))
+        W_in[l].copy_(torch.randn((4 * C, C), generator=gen, device=device, dtype=torch.float32) / math.sqrt(C))
+        gen.manual_seed(_torch_seed(w, l, "W_out"))
+        W_out[l].copy_(torch.randn((C, C), generator=gen, device=device, dtype=torch.float32) / math.sqrt(C))
+    return {"x": x, "W_in": W_in, "W_out": W_out}
 
 
 def to_f64(t) -> np.ndarray:
