@@ -24,6 +24,10 @@ __all__ = [
     "SPARSE_BLOCK_K",
     "hybrid_attn_group",
     "hybrid_attn_group_schedule",
+    "hybrid_attn_proj_in",
+    "hybrid_attn_proj_out",
+    "hybrid_attn_block",
+    "block_workspace_bytes",
     "LAYER_KINDS",
 ]
 
@@ -182,3 +186,72 @@ def hybrid_attn_group_schedule():
     kinds = (ctypes.c_int * 4)()
     _check(_lib.load().hybrid_attn_group_schedule(kinds), "hybrid_attn_group_schedule")
     return [LAYER_KINDS[k] for k in kinds]
+
+
+def _check_weight(name, t, shape, ref):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != ref.dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {tuple(shape)} / {ref.dtype}, got {tuple(t.shape)} / {t.dtype}")
+
+
+def _block_dims(x, heads):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, N, C] device tensor")
+    B, N, C = x.shape
+    if heads <= 0 or C % heads:
+        raise ValueError(f"heads={heads} must divide C={C}")
+    return B, N, C, C // heads
+
+
+def block_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.load().hybrid_attn_block_workspace_bytes(B, H, N, d, code))
+
+
+def hybrid_attn_proj_in(x, W_in, heads, Q=None, K=None, V=None, G=None, stream=None):
+    """Q, K, V, G [B, H, N, d] = the four C-wide blocks of x W_in^T split into
+    `heads` heads; x: [B, N, C], W_in: [4C, C]."""
+    B, N, C, d = _block_dims(x, heads)
+    _check_weight("W_in", W_in, (4 * C, C), x)
+    outs = [torch.empty((B, heads, N, d), dtype=x.dtype, device=x.device) if t is None else t
+            for t in (Q, K, V, G)]
+    _tensors(("Q", "K", "V", "G"), outs, 4)
+    _check(_lib.load().hybrid_attn_proj_in(_ptr(x), _ptr(W_in), *(_ptr(t) for t in outs), B, heads, N, d,
+                                           _dtype_code(x), _stream(stream)),
+           "hybrid_attn_proj_in")
+    return tuple(outs)
+
+
+def hybrid_attn_proj_out(O, W_out, x, x_out=None, stream=None):
+    """x_out = x + concat_heads(O) W_out^T; O: [B, H, N, d], W_out: [C, C],
+    x: [B, N, C].  Pass x_out=x to update x in place."""
+    _tensors(("O",), (O,), 4)
+    B, H, N, d = O.shape
+    _block_dims(x, H)
+    if tuple(x.shape) != (B, N, H * d) or x.dtype != O.dtype:
+        raise ValueError(f"x: expected {(B, N, H * d)} / {O.dtype}, got {tuple(x.shape)} / {x.dtype}")
+    _check_weight("W_out", W_out, (H * d, H * d), x)
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    _check(_lib.load().hybrid_attn_proj_out(_ptr(O), _ptr(W_out), _ptr(x), _ptr(x_out), B, H, N, d,
+                                            _dtype_code(x), _stream(stream)),
+           "hybrid_attn_proj_out")
+    return x_out
+
+
+def hybrid_attn_block(x, W_in4, W_out4, heads, x_out=None, workspace=None, stream=None):
+    """The attention block: four sub-layers (linear, linear, linear, softmax),
+    each x = x + concat_heads(layer(split(x W_in[l]^T))) W_out[l]^T.  x: [B, N, C],
+    W_in4: [4, 4C, C], W_out4: [4, C, C].  Pass x_out=x to update in place."""
+    B, N, C, d = _block_dims(x, heads)
+    _check_weight("W_in4", W_in4, (4, 4 * C, C), x)
+    _check_weight("W_out4", W_out4, (4, C, C), x)
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    need = block_workspace_bytes(B, heads, N, d, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().hybrid_attn_block(_ptr(x), _ptr(W_in4), _ptr(W_out4), _ptr(x_out), B, heads, N, d,
+                                         _dtype_code(x), _ptr(workspace), nbytes, _stream(stream)),
+           "hybrid_attn_block")
+    return x_out

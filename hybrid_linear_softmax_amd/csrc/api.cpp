@@ -84,6 +84,59 @@ int run_linear(const Problem& p, const void* Q, const void* K, const void* V, co
   return hip_status(e);
 }
 
+// Null, alignment and aliasing checks of inputs and outputs of different
+// sizes: no output may overlap an input or another output.
+int check_io(const void* const* in, const size_t* in_bytes, int n_in, void* const* out,
+             const size_t* out_bytes, int n_out) {
+  for (int i = 0; i < n_in; ++i)
+    if (in[i] == nullptr) return HA_EINVAL;
+  for (int i = 0; i < n_out; ++i)
+    if (out[i] == nullptr) return HA_EINVAL;
+  for (int i = 0; i < n_in; ++i)
+    if (misaligned(in[i])) return HA_EALIGN;
+  for (int i = 0; i < n_out; ++i)
+    if (misaligned(out[i])) return HA_EALIGN;
+  for (int j = 0; j < n_out; ++j) {
+    for (int i = 0; i < n_in; ++i)
+      if (overlaps(in[i], in_bytes[i], out[j], out_bytes[j])) return HA_EINVAL;
+    for (int i = 0; i < j; ++i)
+      if (overlaps(out[i], out_bytes[i], out[j], out_bytes[j])) return HA_EINVAL;
+  }
+  return HA_OK;
+}
+
+// Device workspace of the attention block: Q, K, V, G, O of one sub-layer,
+// then the linear layer's workspace (256-byte aligned pieces).
+struct BlockWs {
+  size_t q, k, v, g, o, lin, lin_bytes, total;
+};
+
+BlockWs block_ws(const Problem& p) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  BlockWs w{};
+  size_t off = 0;
+  w.q = off;
+  off += up(p.tensor_bytes);
+  w.k = off;
+  off += up(p.tensor_bytes);
+  w.v = off;
+  off += up(p.tensor_bytes);
+  w.g = off;
+  off += up(p.tensor_bytes);
+  w.o = off;
+  off += up(p.tensor_bytes);
+  w.lin = off;
+  w.lin_bytes = ha::linear_ws(p.BH, p.N, static_cast<int>(p.d), p.bf16).total;
+  off += w.lin_bytes;
+  w.total = off;
+  return w;
+}
+
+size_t weight_bytes(const Problem& p, int64_t rows) {
+  const int64_t C = p.H * p.d;
+  return static_cast<size_t>(rows) * static_cast<size_t>(C) * (p.bf16 ? 2u : 4u);
+}
+
 }  // namespace
 
 namespace ha {
@@ -260,6 +313,92 @@ HA_API int hybrid_attn_group(const void* Q4, const void* K4, const void* V4, con
                              size_t workspace_bytes, hipStream_t stream) {
   return hybrid_attn_group_timed(Q4, K4, V4, G4, O4, B, H, N, d, dtype, workspace, workspace_bytes,
                                  stream, nullptr);
+}
+
+HA_API int hybrid_attn_proj_in(const void* x, const void* W_in, void* Q, void* K, void* V, void* G,
+                               int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const int64_t C = p.H * p.d;
+  const void* in[2] = {x, W_in};
+  const size_t in_bytes[2] = {p.tensor_bytes, weight_bytes(p, 4 * C)};
+  void* out[4] = {Q, K, V, G};
+  const size_t out_bytes[4] = {p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes};
+  st = check_io(in, in_bytes, 2, out, out_bytes, 4);
+  if (st != HA_OK) return st;
+  return hip_status(ha::launch_proj_in(p.bf16, x, W_in, Q, K, V, G, p.B, p.H, p.N, d, stream));
+}
+
+HA_API int hybrid_attn_proj_out(const void* O, const void* W_out, const void* x, void* x_out, int B, int H,
+                                int64_t N, int d, ha_dtype dtype, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const int64_t C = p.H * p.d;
+  // x_out may be x itself; otherwise it must not overlap x
+  const bool in_place = x_out == x;
+  const void* in[3] = {O, W_out, x};
+  const size_t in_bytes[3] = {p.tensor_bytes, weight_bytes(p, C), p.tensor_bytes};
+  void* out[1] = {x_out};
+  const size_t out_bytes[1] = {p.tensor_bytes};
+  st = check_io(in, in_bytes, in_place ? 2 : 3, out, out_bytes, 1);
+  if (st != HA_OK) return st;
+  if (in_place && (x == nullptr || misaligned(x))) return x == nullptr ? HA_EINVAL : HA_EALIGN;
+  return hip_status(ha::launch_proj_out(p.bf16, O, W_out, x, x_out, p.B, p.H, p.N, d, stream));
+}
+
+HA_API size_t hybrid_attn_block_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype) {
+  Problem p;
+  if (check_shape(B, H, N, d, dtype, &p) != HA_OK || p.BH == 0) return 0;
+  return block_ws(p).total;
+}
+
+HA_API int hybrid_attn_block(const void* x, const void* W_in4, const void* W_out4, void* x_out, int B,
+                             int H, int64_t N, int d, ha_dtype dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const int64_t C = p.H * p.d;
+  const size_t win_bytes = weight_bytes(p, 4 * C), wout_bytes = weight_bytes(p, C);
+  const bool in_place = x_out == x;
+  const void* in[3] = {W_in4, W_out4, x};
+  const size_t in_bytes[3] = {4 * win_bytes, 4 * wout_bytes, p.tensor_bytes};
+  void* out[1] = {x_out};
+  const size_t out_bytes[1] = {p.tensor_bytes};
+  st = check_io(in, in_bytes, in_place ? 2 : 3, out, out_bytes, 1);
+  if (st != HA_OK) return st;
+  if (in_place && (x == nullptr || misaligned(x))) return x == nullptr ? HA_EINVAL : HA_EALIGN;
+  const BlockWs L = block_ws(p);
+  if (workspace == nullptr || workspace_bytes < L.total) return HA_EWORKSPACE;
+  if (misaligned(workspace)) return HA_EALIGN;
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(workspace, L.total, in[i], in_bytes[i])) return HA_EINVAL;
+  if (overlaps(workspace, L.total, x_out, p.tensor_bytes)) return HA_EINVAL;
+
+  char* w = static_cast<char*>(workspace);
+  void *q = w + L.q, *k = w + L.k, *v = w + L.v, *g = w + L.g, *o = w + L.o, *lin = w + L.lin;
+  int kinds[4];
+  hybrid_attn_group_schedule(kinds);
+  for (int l = 0; l < 4; ++l) {
+    const void* xin = l == 0 ? x : x_out;
+    const char* wi = static_cast<const char*>(W_in4) + static_cast<size_t>(l) * win_bytes;
+    const char* wo = static_cast<const char*>(W_out4) + static_cast<size_t>(l) * wout_bytes;
+    st = hip_status(ha::launch_proj_in(p.bf16, xin, wi, q, k, v, g, p.B, p.H, p.N, d, stream));
+    if (st != HA_OK) return st;
+    if (kinds[l] == 0)
+      st = run_linear(p, q, k, v, g, o, lin, stream);
+    else
+      st = hip_status(ha::launch_anchor(p.bf16, d, q, k, v, g, o, p.BH, p.N, stream));
+    if (st != HA_OK) return st;
+    st = hip_status(ha::launch_proj_out(p.bf16, o, wo, xin, x_out, p.B, p.H, p.N, d, stream));
+    if (st != HA_OK) return st;
+  }
+  return HA_OK;
 }
 
 HA_API int hybrid_attn_group_schedule(int kinds[4]) {

@@ -50,4 +50,11 @@ hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const v
                          const int32_t* blk_off = nullptr, const int32_t* blk_idx = nullptr,
                          int64_t n_idx = 0);
 
+// Block projections: Q, K, V, G = split_heads(x W_in^T) and
+// x_out = x + concat_heads(O) W_out^T (x_out may be x).
+hipError_t launch_proj_in(bool bf16, const void* x, const void* W_in, void* Q, void* K, void* V, void* G,
+                          int64_t B, int64_t H, int64_t N, int d, hipStream_t s);
+hipError_t launch_proj_out(bool bf16, const void* O, const void* W_out, const void* x, void* x_out,
+                           int64_t B, int64_t H, int64_t N, int d, hipStream_t s);
+
 }  // namespace ha

@@ -152,6 +152,46 @@ HA_API int hybrid_attn_group_timed(const void* Q4, const void* K4, const void* V
                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
                                    hipEvent_t const events[5]);
 
+/* ---- Attention block around the group --------------------------------------
+ * The hybrid layers sit inside DiT blocks (review page, section 3: the compiled
+ * DiT forward; summary page, section 03: the 3:1 interleave).  The block here is
+ * four attention sub-layers on a residual stream x, a dense row-major
+ * [B, N, C] array with C = H * d, sub-layer l of the group's kind l:
+ *     [Q | K | V | G] = x W_in[l]^T            W_in[l]: row-major [4C, C]
+ *     O = gated linear or softmax layer (Q, K, V, G)
+ *     x = x + concat_h(O) W_out[l]^T           W_out[l]: row-major [C, C]
+ * Weights are in the [output feature, input feature] layout.  Output feature
+ * t*C + h*d + e of W_in's product is feature e of head h of tensor t (Q, K, V,
+ * G in that order); column h*d + e of the concatenation is feature e of head h
+ * of O.  Q, K, V, G, O are [B, H, N, d] as above.  The pages print neither the
+ * projections nor the residual; this is the plainest reading.  Products are
+ * taken on the MFMA in bf16 with float32 accumulation (float32 throughout for
+ * HA_F32); results are rounded once, on store. */
+
+/* Q, K, V, G = the four C-wide blocks of x W_in^T, split into heads.  x: [B, N, C],
+ * W_in: [4C, C]; outputs [B, H, N, d], none overlapping another buffer. */
+HA_API int hybrid_attn_proj_in(const void* x, const void* W_in, void* Q, void* K, void* V, void* G,
+                               int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream);
+
+/* x_out = x + concat_h(O) W_out^T.  O: [B, H, N, d], W_out: [C, C], x, x_out:
+ * [B, N, C].  x_out may be x itself (in place); otherwise it must not overlap
+ * any input. */
+HA_API int hybrid_attn_proj_out(const void* O, const void* W_out, const void* x, void* x_out,
+                                int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream);
+
+/* Bytes of device workspace hybrid_attn_block needs: Q, K, V, G, O of one
+ * sub-layer plus the linear layer's workspace.  0 for an empty or invalid problem. */
+HA_API size_t hybrid_attn_block_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype);
+
+/* The block: the four sub-layers in order on one stream.  W_in4: [4, 4C, C],
+ * W_out4: [4, C, C].  x_out may be x (in place); the workspace must not overlap
+ * x, x_out or the weights.  Each stage is the same kernel as the matching
+ * single entry point, so the result is bitwise equal to calling
+ * hybrid_attn_proj_in, the layer and hybrid_attn_proj_out in turn. */
+HA_API int hybrid_attn_block(const void* x, const void* W_in4, const void* W_out4, void* x_out,
+                             int B, int H, int64_t N, int d, ha_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Writes the layer kinds of a group in order: 0 = gated linear, 1 = gated
  * softmax anchor; i.e. {0, 0, 0, 1}.  Returns HA_EINVAL for a NULL array. */
 HA_API int hybrid_attn_group_schedule(int kinds[4]);

@@ -17,4 +17,4 @@ from .hybrid_ref import (  # noqa: F401
     layer,
     group,
 )
-from .block_ref import block, merge_heads, project_in, project_out, split_heads  # noqa: F401
+from .block_ref import block, merge_heads, project_in, project_out, round_bf16, split_heads  # noqa: F401

@@ -57,12 +57,26 @@ def project_out(O, W_out, x):
     return x + merge_heads(O) @ W_out.T
 
 
-def block(x, W_in4, W_out4, H, kinds=SCHEDULE):
-    """The four sub-layers in order; W_in4 [L, 4C, C], W_out4 [L, C, C]."""
+def round_bf16(a):
+    """Round to the nearest bfloat16 (ties to even) by way of float32, the
+    storage format of a bf16 tensor: keep the top 16 bits of the float32
+    pattern after adding 0x7FFF plus the lowest kept bit.  Returns float64."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def block(x, W_in4, W_out4, H, kinds=SCHEDULE, store=None):
+    """The four sub-layers in order; W_in4 [L, 4C, C], W_out4 [L, C, C].
+
+    `store`, when given, is applied to every tensor the block hands from one
+    stage to the next (Q, K, V, G, O and the updated x): round_bf16 models a
+    path that keeps those tensors in bfloat16 while its arithmetic is exact."""
     x = np.asarray(x, dtype=np.float64)
+    keep = (lambda a: a) if store is None else store
     if len(W_in4) != len(kinds) or len(W_out4) != len(kinds):
         raise ValueError(f"{len(kinds)} layers need {len(kinds)} weight pairs")
     for l, kind in enumerate(kinds):
-        Q, K, V, G = project_in(x, W_in4[l], H)
-        x = project_out(layer(kind, Q, K, V, G), W_out4[l], x)
+        Q, K, V, G = (keep(t) for t in project_in(x, W_in4[l], H))
+        x = keep(project_out(keep(layer(kind, Q, K, V, G)), W_out4[l], x))
     return x

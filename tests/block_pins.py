@@ -178,7 +178,34 @@ def pin_block_is_composition_in_order(impl):
     assert _rel(rev, want) > 1e-6
 
 
+def pin_round_bf16_matches_library(impl):
+    """The storage rounding against torch's float32 -> bfloat16 conversion (round
+    to nearest even) on random values of every magnitude and on exact ties."""
+    import torch
+    r = np.random.default_rng(28)
+    v = (r.standard_normal(20000) * np.exp2(r.integers(-30, 30, 20000))).astype(np.float32)
+    ties = (np.arange(1, 4001, dtype=np.uint32) << 16 | 0x8000).view(np.float32)   # half-way bit patterns
+    for a in (v, ties, -ties, np.array([0.0, -0.0, 1.0, 65504.0, 1e-38], dtype=np.float32)):
+        want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+        assert np.array_equal(impl.round_bf16(a), want)
+
+
+def pin_storage_rounding_is_applied(impl):
+    """With a storage rounding the block differs from the exact one by a few
+    bf16 ulps of the stream, and identity storage changes nothing."""
+    B, N, H, d = 1, 16, 2, 4
+    x = np.random.default_rng(29).standard_normal((B, N, H * d))
+    Wi, Wo = _weights(30, 4, H * d)
+    exact = impl.block(x, Wi, Wo, H)
+    assert np.array_equal(impl.block(x, Wi, Wo, H, store=lambda a: a), exact)
+    rounded = impl.block(x, Wi, Wo, H, store=impl.round_bf16)
+    assert 0 < _rel(rounded, exact) < 2.0 ** -5
+    assert np.array_equal(impl.round_bf16(rounded), rounded)   # the stream is stored
+
+
 ALL_PINS = [
+    pin_round_bf16_matches_library,
+    pin_storage_rounding_is_applied,
     pin_project_in_loops,
     pin_project_out_loops,
     pin_zero_output_projection_is_identity,

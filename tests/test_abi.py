@@ -134,3 +134,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_projection_errors(lib):
+    # (only rejected calls: a valid one would launch on the fake addresses)
+    def pin_(x=Q, w=K, q=O, k=S, v=Z, g=OFF, d=64, dt=HA_BF16, H=2):
+        return lib.hybrid_attn_proj_in(x, w, q, k, v, g, 1, H, 100, d, dt, None)
+
+    assert pin_(d=96) == EUNSUP and pin_(dt=7) == EUNSUP
+    assert pin_(H=-1) == EINVAL
+    assert pin_(x=None) == EINVAL and pin_(g=None) == EINVAL
+    assert pin_(w=K + 8) == EALIGN and pin_(v=Z + 4) == EALIGN
+    assert pin_(q=Q) == EINVAL                      # an output aliases x
+    assert pin_(k=K + 4096) == EINVAL               # an output overlaps W_in
+    assert pin_(k=O) == EINVAL                      # two outputs alias
+    assert lib.hybrid_attn_proj_in(Q, K, O, S, Z, OFF, 1, 2, 0, 64, HA_BF16, None) == OK
+
+    def pout(o=Q, w=K, x=V, xo=O, d=64):
+        return lib.hybrid_attn_proj_out(o, w, x, xo, 1, 2, 100, d, HA_BF16, None)
+
+    assert pout(d=80) == EUNSUP
+    assert pout(o=None) == EINVAL and pout(xo=None) == EINVAL
+    assert pout(xo=V + 64) == EINVAL                # overlaps x without being x
+    assert pout(xo=Q + 16) == EINVAL                # overlaps O
+    assert pout(w=K + 2) == EALIGN
+
+
+def test_block_errors(lib):
+    w = lib.hybrid_attn_block_workspace_bytes
+    need = w(1, 2, 100, 64, HA_BF16)
+    assert need > 5 * 100 * 128 * 2 and w(1, 2, 100, 64, HA_BF16) == need
+    assert w(1, 2, 100, 96, HA_BF16) == 0 and w(0, 2, 100, 64, HA_BF16) == 0
+
+    def blk(x=Q, wi=K, wo=V, xo=O, ws=WS, nb=need, d=64):
+        return lib.hybrid_attn_block(x, wi, wo, xo, 1, 2, 100, d, HA_BF16, ws, nb, None)
+
+    assert blk(d=32) == EUNSUP
+    assert blk(wi=None) == EINVAL
+    assert blk(xo=K + 128) == EINVAL                # output overlaps the input weights
+    assert blk(ws=None) == EWS and blk(nb=need - 1) == EWS
+    assert blk(ws=WS + 4) == EALIGN
+    assert blk(ws=Q - 1024) == EINVAL               # workspace overlaps x
+    assert blk(ws=O - 4096) == EINVAL               # workspace overlaps x_out
+    assert lib.hybrid_attn_block(Q, K, V, O, 1, 2, 0, 64, HA_BF16, None, 0, None) == OK

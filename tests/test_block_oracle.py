@@ -10,8 +10,18 @@ from oracle import block_ref as R
 from oracle import hybrid_ref
 
 
+def _truncate_bf16(a):
+    u = np.asarray(a, dtype=np.float32).view(np.uint32)
+    return ((u >> 16) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _round_half_up_bf16(a):
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return (((u + 0x8000) >> 16) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def _impl(split=R.split_heads, merge=R.merge_heads, order=(0, 1, 2, 3), transpose_out=True,
-          residual=True, stack="sequential"):
+          residual=True, stack="sequential", rounding=R.round_bf16):
     def project_in(x, W_in, H):
         x = np.asarray(x, dtype=np.float64)
         C = x.shape[-1]
@@ -24,7 +34,8 @@ def _impl(split=R.split_heads, merge=R.merge_heads, order=(0, 1, 2, 3), transpos
         y = merge(np.asarray(O, dtype=np.float64)) @ (W.T if transpose_out else W)
         return (np.asarray(x, dtype=np.float64) + y) if residual else y
 
-    def block(x, W_in4, W_out4, H, kinds=hybrid_ref.SCHEDULE):
+    def block(x, W_in4, W_out4, H, kinds=hybrid_ref.SCHEDULE, store=None):
+        keep = (lambda a: a) if store is None else store
         x = np.asarray(x, dtype=np.float64)
         x0 = x
         layers = list(enumerate(kinds))
@@ -33,11 +44,12 @@ def _impl(split=R.split_heads, merge=R.merge_heads, order=(0, 1, 2, 3), transpos
         for l, kind in layers:
             src = x0 if stack == "parallel" else x
             Wi = W_in4[0] if stack == "shared_in" else W_in4[l]
-            Q, K, V, G = project_in(src, Wi, H)
-            x = project_out(hybrid_ref.layer(kind, Q, K, V, G), W_out4[l], x)
+            Q, K, V, G = (keep(t) for t in project_in(src, Wi, H))
+            x = keep(project_out(keep(hybrid_ref.layer(kind, Q, K, V, G)), W_out4[l], x))
         return x
 
-    return types.SimpleNamespace(project_in=project_in, project_out=project_out, block=block)
+    return types.SimpleNamespace(project_in=project_in, project_out=project_out, block=block,
+                                 round_bf16=rounding)
 
 
 @pytest.mark.parametrize("pin", block_pins.ALL_PINS, ids=lambda p: p.__name__)
@@ -66,6 +78,8 @@ MUTANTS = {
     "sub-layers read the block input": _impl(stack="parallel"),
     "sub-layers in reverse order": _impl(stack="reversed"),
     "one input projection for all": _impl(stack="shared_in"),
+    "bf16 storage truncates": _impl(rounding=_truncate_bf16),
+    "bf16 storage rounds ties up": _impl(rounding=_round_half_up_bf16),
 }
 
 
