@@ -16,6 +16,11 @@ workload.  Extra fields: per-layer milliseconds and the all-softmax group
 kernel over the LVSA frame pattern of the workload's latent grid (a window of
 frames plus periodic global frames), the three linear layers unchanged; the
 extra field then compares against one dense anchor on the same inputs.
+
+--mode block measures the attention block around the group instead: a step is
+hybrid_attn_block on a residual stream x [B, N, H*d] with synthetic weights
+(four sub-layers, each Q/K/V/G projection, the layer, output projection and
+residual); one extra untimed-for-value pass times each stage on its own.
 """
 import argparse
 import hashlib
@@ -126,6 +131,155 @@ def pattern_pairs(N, offsets, indices, only=None):
     return total
 
 
+def block_cpu_baseline(w, blk, rows_sampled: int):
+    """The oracle timed on a sample of one block: the two projections of
+    `rows_sampled` token rows (rows are independent), the linear layer of one
+    head and `rows_sampled` anchor rows of one head, extrapolated to the block."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import to_f64
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"],
+                  default=1)
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(w.N, size=min(rows_sampled, w.N), replace=False))
+    x = to_f64(blk["x"][:1, rows])
+    Wi, Wo = to_f64(blk["W_in"][0]), to_f64(blk["W_out"][0])
+    t0 = time.perf_counter()
+    Q, K, V, G = oracle.project_in(x, Wi, w.H)
+    oracle.project_out(Q, Wo, x)
+    t_proj = time.perf_counter() - t0
+    # attention on the projected rows of head 0, scaled to the full sequence
+    from workloads import layer_inputs_host
+    att = layer_inputs_host(w, 3, B=1, H=1, N=w.N)
+    q, k, v, g = (to_f64(att[n][0, 0]) for n in "QKVG")
+    t0 = time.perf_counter()
+    oracle.linear_attention(q, k, v, g)
+    t_lin = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.softmax_attention(q, k, v, g, rows=rows)
+    t_rows = time.perf_counter() - t0
+    heads = w.B * w.H
+    t_block = 4 * t_proj * (w.B * w.N / rows.size) + 3 * heads * t_lin + heads * (w.N / rows.size) * t_rows
+    return {
+        "value": w.B * w.N / t_block,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: projections of {rows.size} token rows ({t_proj:.2f} s), the linear "
+                   f"layer of 1 of {heads} heads ({t_lin:.2f} s) and {rows.size} anchor rows of 1 head "
+                   f"({t_rows:.2f} s), extrapolated to 4 sub-layers ({t_block:.0f} s per block)"),
+    }
+
+
+def run_block(args, w):
+    import torch
+
+    import hybrid_linear_softmax_amd as ha
+    from workloads import block_inputs_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    C = w.H * w.d
+    M = w.B * w.N
+    print(f"[bench] block {w.name}: B={w.B} N={w.N} C={C} (H={w.H} x d={w.d}); generating inputs",
+          file=sys.stderr, flush=True)
+    blk = block_inputs_device(w, dev)
+    x, Wi, Wo = blk["x"], blk["W_in"], blk["W_out"]
+    x_out = torch.empty_like(x)
+    ws = torch.empty(ha.block_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        ha.hybrid_attn_block(x, Wi, Wo, w.H, x_out=x_out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} block steps", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-stage breakdown: the same kernels called one stage at a time
+    Q, K, V, G = (torch.empty((w.B, w.H, w.N, w.d), dtype=x.dtype, device=dev) for _ in range(4))
+    O = torch.empty_like(Q)
+    lin_ws = torch.empty(ha.workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    y = x.clone()
+    stage = {"proj_in": 0.0, "linear": 0.0, "softmax": 0.0, "proj_out": 0.0}
+    reps = max(1, min(args.steps, 3))
+    for _ in range(reps):
+        y.copy_(x)
+        for l, kind in enumerate(ha.hybrid_attn_group_schedule()):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            ha.hybrid_attn_proj_in(y, Wi[l], w.H, Q, K, V, G)
+            ev[1].record()
+            if kind == "linear":
+                ha.hybrid_attn_linear(Q, K, V, G, O, workspace=lin_ws)
+            else:
+                ha.hybrid_attn_softmax(Q, K, V, G, O)
+            ev[2].record()
+            ha.hybrid_attn_proj_out(O, Wo[l], y, x_out=y)
+            ev[3].record()
+            torch.cuda.synchronize()
+            stage["proj_in"] += ev[0].elapsed_time(ev[1]) / reps / 4
+            stage[kind] += ev[1].elapsed_time(ev[2]) / reps / (3 if kind == "linear" else 1)
+            stage["proj_out"] += ev[2].elapsed_time(ev[3]) / reps / 4
+    fl_in, fl_out = 2.0 * M * C * 4 * C, 2.0 * M * C * C
+    anchor_flop = 4.0 * w.B * w.H * w.N * w.N * w.d
+    anchor_tf = anchor_flop / (stage["softmax"] / 1e3) / 1e12
+    roofline = {
+        "kernel": "anchor_bf16 (gated softmax anchor, the block's dominant kernel)",
+        "bound": "mfma",
+        "achieved": round(anchor_tf, 1),
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(anchor_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": None,
+    }
+    gemm = {
+        "proj_in_ms": round(stage["proj_in"], 3),
+        "proj_in_tflops": round(fl_in / (stage["proj_in"] / 1e3) / 1e12, 1),
+        "proj_out_ms": round(stage["proj_out"], 3),
+        "proj_out_tflops": round(fl_out / (stage["proj_out"] / 1e3) / 1e12, 1),
+    }
+    gemm["proj_in_frac"] = round(gemm["proj_in_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    gemm["proj_out_frac"] = round(gemm["proj_out_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = block_cpu_baseline(w, blk, args.cpu_rows)
+    line = {
+        "metric": "attention block (4 projected sub-layers around the 3:1 group) tokens/s",
+        "value": round(M / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_block", "B": w.B, "N": w.N, "H": w.H, "d": w.d, "C": C,
+                   "sublayers": "linear,linear,linear,softmax", "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stage_ms": {k: round(v, 3) for k, v in stage.items()},
+        "projections": gemm,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +292,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048, help="softmax rows the oracle baseline samples")
     ap.add_argument("--anchor", choices=("dense", "lvsa"), default="dense",
                     help="dense softmax anchor (default) or the block-sparse LVSA anchor")
+    ap.add_argument("--mode", choices=("group", "block"), default="group",
+                    help="the hybrid group (default) or the attention block around it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -155,6 +311,8 @@ def main():
     w = get(args.config)
     if w.dtype != "bf16":
         raise SystemExit("bench workloads are the bf16 shapes; the fp32 tiny shape is a test case")
+    if args.mode == "block":
+        return run_block(args, w)
     sparse = args.anchor == "lvsa"
     label = f"{w.name}_lvsa" if sparse else w.name
     pattern = None
