@@ -18,3 +18,11 @@ from .hybrid_ref import (  # noqa: F401
     group,
 )
 from .block_ref import block, merge_heads, project_in, project_out, round_bf16, split_heads  # noqa: F401
+from .backward_ref import (  # noqa: F401
+    layer_backward,
+    linear_attention_backward,
+    softmax_attention_backward,
+    softmax_attention_backward_keys,
+    softmax_attention_backward_rows,
+    softmax_lse,
+)
