@@ -24,6 +24,8 @@ __all__ = [
     "SPARSE_BLOCK_K",
     "hybrid_attn_group",
     "hybrid_attn_group_schedule",
+    "hybrid_attn_linear_backward",
+    "linear_backward_workspace_bytes",
     "hybrid_attn_proj_in",
     "hybrid_attn_proj_out",
     "hybrid_attn_block",
@@ -255,3 +257,26 @@ def hybrid_attn_block(x, W_in4, W_out4, heads, x_out=None, workspace=None, strea
                                          _dtype_code(x), _ptr(workspace), nbytes, _stream(stream)),
            "hybrid_attn_block")
     return x_out
+
+
+def linear_backward_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.load().hybrid_attn_linear_backward_workspace_bytes(B, H, N, d, code))
+
+
+def hybrid_attn_linear_backward(Q, K, V, G, dO, grads=None, workspace=None, stream=None):
+    """dQ, dK, dV, dG of the gated linear layer for the upstream gradient dO
+    (all [B, H, N, d]).  `grads` may hold four preallocated output tensors."""
+    ref = _tensors(("Q", "K", "V", "G", "dO"), (Q, K, V, G, dO), 4)
+    B, H, N, d = ref.shape
+    grads = [torch.empty_like(ref) for _ in range(4)] if grads is None else list(grads)
+    _tensors(("dQ", "dK", "dV", "dG"), grads, 4)
+    need = linear_backward_workspace_bytes(B, H, N, d, ref.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ref.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().hybrid_attn_linear_backward(*(_ptr(t) for t in (Q, K, V, G, dO)), *(_ptr(t) for t in grads),
+                                                   B, H, N, d, _dtype_code(ref), _ptr(workspace), nbytes,
+                                                   _stream(stream)),
+           "hybrid_attn_linear_backward")
+    return tuple(grads)

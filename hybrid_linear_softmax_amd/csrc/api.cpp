@@ -315,6 +315,37 @@ HA_API int hybrid_attn_group(const void* Q4, const void* K4, const void* V4, con
                                  stream, nullptr);
 }
 
+HA_API size_t hybrid_attn_linear_backward_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype) {
+  Problem p;
+  if (check_shape(B, H, N, d, dtype, &p) != HA_OK || p.BH == 0) return 0;
+  return ha::linear_bwd_ws(p.BH, p.N, d, p.bf16).total;
+}
+
+HA_API int hybrid_attn_linear_backward(const void* Q, const void* K, const void* V, const void* G,
+                                       const void* dO, void* dQ, void* dK, void* dV, void* dG, int B,
+                                       int H, int64_t N, int d, ha_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const void* in[5] = {Q, K, V, G, dO};
+  const size_t in_bytes[5] = {p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes};
+  void* out[4] = {dQ, dK, dV, dG};
+  const size_t out_bytes[4] = {p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes};
+  st = check_io(in, in_bytes, 5, out, out_bytes, 4);
+  if (st != HA_OK) return st;
+  const size_t need = ha::linear_bwd_ws(p.BH, p.N, d, p.bf16).total;
+  if (workspace == nullptr || workspace_bytes < need) return HA_EWORKSPACE;
+  if (misaligned(workspace)) return HA_EALIGN;
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(workspace, need, in[i], in_bytes[i])) return HA_EINVAL;
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(workspace, need, out[i], out_bytes[i])) return HA_EINVAL;
+  return hip_status(ha::launch_linear_backward(p.bf16, d, Q, K, V, G, dO, dQ, dK, dV, dG, p.BH, p.N,
+                                               HA_LINEAR_EPS, workspace, stream));
+}
+
 HA_API int hybrid_attn_proj_in(const void* x, const void* W_in, void* Q, void* K, void* V, void* G,
                                int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream) {
   Problem p;

@@ -29,12 +29,15 @@ struct LinearWs {
 LinearWs linear_ws(int64_t BH, int64_t N, int d, bool bf16);
 
 // R1 pass 1: per (bh, chunk) partial state into part.
+// wz (optional, [BH, N] float32) weights the z sum per token.
 hipError_t launch_kv_partials(bool bf16, int d, const void* K, const void* V, float* part,
-                              int64_t BH, int64_t N, KvSplit split, hipStream_t s);
+                              int64_t BH, int64_t N, KvSplit split, hipStream_t s,
+                              const float* wz = nullptr);
 // R1 pass 2: fixed-order sum over chunks into S, z (and the bf16 hi/lo S^T).
+// S_hi/S_lo (optional, bf16 path) also receive the untransposed hi/lo split.
 hipError_t launch_kv_reduce(bool bf16, int d, const float* part, float* S, float* z,
                             uint16_t* St_hi, uint16_t* St_lo, int64_t BH, int64_t chunks,
-                            hipStream_t s);
+                            hipStream_t s, uint16_t* S_hi = nullptr, uint16_t* S_lo = nullptr);
 // R2: fused apply phi(Q) S / (phi(Q) z + eps), sigmoid gate, store.
 hipError_t launch_apply(bool bf16, int d, const void* Q, const void* G, void* O, const float* S,
                         const float* z, const uint16_t* St_hi, const uint16_t* St_lo, int64_t BH,
@@ -49,6 +52,22 @@ hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const v
                          const void* G, void* O, int64_t BH, int64_t N, hipStream_t s,
                          const int32_t* blk_off = nullptr, const int32_t* blk_idx = nullptr,
                          int64_t n_idx = 0);
+
+// Workspace of the linear layer's backward pass (byte offsets).
+struct LinearBwdWs {
+  size_t part;                    // float [BH][chunks][d*d + d], reused by both reductions
+  size_t S, z, dS, dz;            // float [BH][d][d], [BH][d]
+  size_t St_hi, St_lo, S_hi, S_lo;      // bf16 [BH][d][d] (bf16 path only)
+  size_t dSt_hi, dSt_lo, dS_hi, dS_lo;  // bf16 [BH][d][d] (bf16 path only)
+  size_t dn;                      // [BH][N][d] in the I/O dtype
+  size_t dden;                    // float [BH][N]
+  size_t total;
+};
+LinearBwdWs linear_bwd_ws(int64_t BH, int64_t N, int d, bool bf16);
+// dQ, dK, dV, dG of the gated linear layer given dO (six passes, see linear_bwd.hip).
+hipError_t launch_linear_backward(bool bf16, int d, const void* Q, const void* K, const void* V,
+                                  const void* G, const void* dO, void* dQ, void* dK, void* dV, void* dG,
+                                  int64_t BH, int64_t N, float eps, void* ws, hipStream_t s);
 
 // Block projections: Q, K, V, G = split_heads(x W_in^T) and
 // x_out = x + concat_heads(O) W_out^T (x_out may be x).

@@ -21,11 +21,14 @@ namespace {
 constexpr int kTile = 64;  // tokens per pass-1 tile
 
 // ---------------------------------------------------------------- bf16 pass 1
+// wz (optional, [B*H, N] float32) weights the z sum: z = sum_j wz_j phi(k_j)
+// (the backward pass's dz = sum_i dden_i phi(q_i)); null gives the plain sum.
 template <int D>
 __global__ __launch_bounds__(256) void kv_partials_bf16(const bf16_t* __restrict__ K,
                                                         const bf16_t* __restrict__ V,
                                                         float* __restrict__ part, int64_t N,
-                                                        int64_t chunk_len, int64_t chunks) {
+                                                        int64_t chunk_len, int64_t chunks,
+                                                        const float* __restrict__ wz) {
   constexpr int P = kTile + 8;            // LDS pitch (elements) of a transposed row
   constexpr int FG = D / 8;               // 16-byte feature groups per token row
   constexpr int SUB = (kTile / 4) * FG;   // 4-token x 8-feature sub-tiles per tensor
@@ -104,10 +107,19 @@ __global__ __launch_bounds__(256) void kv_partials_bf16(const bf16_t* __restrict
       if (sub_k[i]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          zacc[0] += bf_lo(w[r].x); zacc[1] += bf_hi(w[r].x);
-          zacc[2] += bf_lo(w[r].y); zacc[3] += bf_hi(w[r].y);
-          zacc[4] += bf_lo(w[r].z); zacc[5] += bf_hi(w[r].z);
-          zacc[6] += bf_lo(w[r].w); zacc[7] += bf_hi(w[r].w);
+          if (wz == nullptr) {
+            zacc[0] += bf_lo(w[r].x); zacc[1] += bf_hi(w[r].x);
+            zacc[2] += bf_lo(w[r].y); zacc[3] += bf_hi(w[r].y);
+            zacc[4] += bf_lo(w[r].z); zacc[5] += bf_hi(w[r].z);
+            zacc[6] += bf_lo(w[r].w); zacc[7] += bf_hi(w[r].w);
+          } else {
+            const int64_t tok = t0 + 4 * sub_m[i] + r;
+            const float wt = tok < t_end ? wz[bh * N + tok] : 0.f;
+            zacc[0] = fmaf(wt, bf_lo(w[r].x), zacc[0]); zacc[1] = fmaf(wt, bf_hi(w[r].x), zacc[1]);
+            zacc[2] = fmaf(wt, bf_lo(w[r].y), zacc[2]); zacc[3] = fmaf(wt, bf_hi(w[r].y), zacc[3]);
+            zacc[4] = fmaf(wt, bf_lo(w[r].z), zacc[4]); zacc[5] = fmaf(wt, bf_hi(w[r].z), zacc[5]);
+            zacc[6] = fmaf(wt, bf_lo(w[r].w), zacc[6]); zacc[7] = fmaf(wt, bf_hi(w[r].w), zacc[7]);
+          }
         }
       }
       uint2 tr[8];
@@ -171,7 +183,8 @@ template <int D>
 __global__ __launch_bounds__(256) void kv_partials_f32(const float* __restrict__ K,
                                                        const float* __restrict__ V,
                                                        float* __restrict__ part, int64_t N,
-                                                       int64_t chunk_len, int64_t chunks) {
+                                                       int64_t chunk_len, int64_t chunks,
+                                                       const float* __restrict__ wz) {
   constexpr int T = 32;
   constexpr int R = D / 16;
   __shared__ __attribute__((aligned(16))) float sK[T][D];
@@ -193,8 +206,10 @@ __global__ __launch_bounds__(256) void kv_partials_f32(const float* __restrict__
 #pragma unroll
     for (int y = 0; y < R; ++y) acc[x][y] = 0.f;
   }
+  __shared__ float sW[T];
   for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
     __syncthreads();
+    if (tid < T) sW[tid] = (t0 + tid < t_end) ? (wz == nullptr ? 1.f : wz[bh * N + t0 + tid]) : 0.f;
     for (int e = tid; e < T * D / 4; e += 256) {
       const int row = e / (D / 4), col = 4 * (e % (D / 4));
       const int64_t tok = t0 + row;
@@ -215,9 +230,10 @@ __global__ __launch_bounds__(256) void kv_partials_f32(const float* __restrict__
       for (int x = 0; x < R; ++x) kr[x] = sK[n][ta + 16 * x];
 #pragma unroll
       for (int y = 0; y < R; ++y) vr[y] = sV[n][tj + 16 * y];
+      const float wt = sW[n];
 #pragma unroll
       for (int x = 0; x < R; ++x) {
-        zacc[x] += kr[x];
+        zacc[x] = fmaf(wt, kr[x], zacc[x]);
 #pragma unroll
         for (int y = 0; y < R; ++y) acc[x][y] = fmaf(kr[x], vr[y], acc[x][y]);
       }
@@ -237,12 +253,15 @@ __global__ __launch_bounds__(256) void kv_partials_f32(const float* __restrict__
 // Element e of (S, z) of one head: sum over chunks in order.  The bf16 path also
 // stores S^T split into bf16 hi + lo (hi = rne(s), lo = rne(s - hi)), the layout
 // the apply kernel's MFMA B operand reads.
+// S_hi / S_lo (optional) receive the same split untransposed ([a][j]), the
+// layout the backward pass's products with S^T read.
 template <int D>
 __global__ __launch_bounds__(256) void kv_reduce(const float* __restrict__ part,
                                                  float* __restrict__ S, float* __restrict__ z,
                                                  bf16_t* __restrict__ St_hi,
                                                  bf16_t* __restrict__ St_lo, int64_t chunks,
-                                                 int blocks_per_head) {
+                                                 int blocks_per_head, bf16_t* __restrict__ S_hi,
+                                                 bf16_t* __restrict__ S_lo) {
   constexpr int E = D * D + D;
   const int64_t bh = blockIdx.x / blocks_per_head;
   const int e = (blockIdx.x % blocks_per_head) * 256 + threadIdx.x;
@@ -256,8 +275,13 @@ __global__ __launch_bounds__(256) void kv_reduce(const float* __restrict__ part,
       const int a = e / D, j = e % D;
       const bf16_t hi = to_bf16(s);
       const float hif = __uint_as_float(static_cast<uint32_t>(hi) << 16);
+      const bf16_t lo = to_bf16(s - hif);
       St_hi[bh * D * D + j * D + a] = hi;
-      St_lo[bh * D * D + j * D + a] = to_bf16(s - hif);
+      St_lo[bh * D * D + j * D + a] = lo;
+      if (S_hi != nullptr) {
+        S_hi[bh * D * D + e] = hi;
+        S_lo[bh * D * D + e] = lo;
+      }
     }
   } else {
     z[bh * D + (e - D * D)] = s;
@@ -279,40 +303,42 @@ KvSplit kv_split(int64_t BH, int64_t N) {
 }
 
 hipError_t launch_kv_partials(bool bf16, int d, const void* K, const void* V, float* part,
-                              int64_t BH, int64_t N, KvSplit sp, hipStream_t s) {
+                              int64_t BH, int64_t N, KvSplit sp, hipStream_t s, const float* wz) {
   if (sp.chunks == 0 || BH == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(BH * sp.chunks)), block(256);
   if (bf16) {
     const bf16_t* k = static_cast<const bf16_t*>(K);
     const bf16_t* v = static_cast<const bf16_t*>(V);
     if (d == 128)
-      kv_partials_bf16<128><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+      kv_partials_bf16<128><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks, wz);
     else
-      kv_partials_bf16<64><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+      kv_partials_bf16<64><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks, wz);
   } else {
     const float* k = static_cast<const float*>(K);
     const float* v = static_cast<const float*>(V);
     if (d == 128)
-      kv_partials_f32<128><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+      kv_partials_f32<128><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks, wz);
     else
-      kv_partials_f32<64><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks);
+      kv_partials_f32<64><<<grid, block, 0, s>>>(k, v, part, N, sp.chunk_len, sp.chunks, wz);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_kv_reduce(bool bf16, int d, const float* part, float* S, float* z,
                             uint16_t* St_hi, uint16_t* St_lo, int64_t BH, int64_t chunks,
-                            hipStream_t s) {
+                            hipStream_t s, uint16_t* S_hi, uint16_t* S_lo) {
   if (BH == 0) return hipSuccess;
   const int E = d * d + d;
   const int bph = (E + 255) / 256;
   const dim3 grid(static_cast<unsigned>(BH * bph)), block(256);
   bf16_t* hi = bf16 ? St_hi : nullptr;
   bf16_t* lo = bf16 ? St_lo : nullptr;
+  bf16_t* shi = bf16 && St_hi != nullptr ? S_hi : nullptr;
+  bf16_t* slo = bf16 && St_hi != nullptr ? S_lo : nullptr;
   if (d == 128)
-    kv_reduce<128><<<grid, block, 0, s>>>(part, S, z, hi, lo, chunks, bph);
+    kv_reduce<128><<<grid, block, 0, s>>>(part, S, z, hi, lo, chunks, bph, shi, slo);
   else
-    kv_reduce<64><<<grid, block, 0, s>>>(part, S, z, hi, lo, chunks, bph);
+    kv_reduce<64><<<grid, block, 0, s>>>(part, S, z, hi, lo, chunks, bph, shi, slo);
   return hipGetLastError();
 }
 

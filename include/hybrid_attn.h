@@ -152,6 +152,29 @@ HA_API int hybrid_attn_group_timed(const void* Q4, const void* K4, const void* V
                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
                                    hipEvent_t const events[5]);
 
+/* ---- Backward pass ----------------------------------------------------------
+ * The model is trained from scratch (review page, section 3; news item,
+ * "Prestaties"), so each layer has a backward pass: given dO = dL/dO it returns
+ * dQ, dK, dV, dG (all [B, H, N, d] of `dtype`, the inputs' layout).  The
+ * gradients follow the forward formulas above by the chain rule, with the
+ * ReLU's derivative taken as 0 at 0; they are exact up to rounding (bf16
+ * operands, float32 accumulation).  Outputs must not overlap any input or each
+ * other.  Deterministic: fixed reduction orders, no atomics. */
+
+/* Bytes of device workspace hybrid_attn_linear_backward needs (pure function;
+ * 0 for an empty or invalid problem). */
+HA_API size_t hybrid_attn_linear_backward_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype);
+
+/* Backward pass of the gated linear layer.  Recomputes the state S, z from K, V
+ * and streams every token four more times: dG, dn = sigmoid(g) dO / den and
+ * dden = -(sigmoid(g) dO . a) / den per token; dS = sum phi(q)^T dn and
+ * dz = sum dden phi(q) (deterministic split-N reduction); then
+ * dQ = (dn S^T + dden z) [Q > 0], dV = phi(K) dS, dK = (V dS^T + dz) [K > 0]. */
+HA_API int hybrid_attn_linear_backward(const void* Q, const void* K, const void* V, const void* G,
+                                       const void* dO, void* dQ, void* dK, void* dV, void* dG,
+                                       int B, int H, int64_t N, int d, ha_dtype dtype,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- Attention block around the group --------------------------------------
  * The hybrid layers sit inside DiT blocks (review page, section 3: the compiled
  * DiT forward; summary page, section 03: the 3:1 interleave).  The block here is

@@ -177,3 +177,22 @@ def test_block_errors(lib):
     assert blk(ws=Q - 1024) == EINVAL               # workspace overlaps x
     assert blk(ws=O - 4096) == EINVAL               # workspace overlaps x_out
     assert lib.hybrid_attn_block(Q, K, V, O, 1, 2, 0, 64, HA_BF16, None, 0, None) == OK
+
+
+def test_linear_backward_errors(lib):
+    need = lib.hybrid_attn_linear_backward_workspace_bytes(1, 2, 100, 64, HA_BF16)
+    assert need > 0 and lib.hybrid_attn_linear_backward_workspace_bytes(1, 2, 100, 96, HA_BF16) == 0
+    DQ, DK, DV, DG, DO = (GB * (20 + i) for i in range(5))
+
+    def bwd(q=Q, dq=DQ, dk=DK, do=DO, ws=WS, nb=need, d=64):
+        return lib.hybrid_attn_linear_backward(q, K, V, G, do, dq, dk, DV, DG, 1, 2, 100, d, HA_BF16, ws, nb, None)
+
+    assert bwd(d=80) == EUNSUP
+    assert bwd(do=None) == EINVAL and bwd(dq=None) == EINVAL
+    assert bwd(dq=Q) == EINVAL                     # a gradient aliases an input
+    assert bwd(dk=DQ + 64) == EINVAL               # two gradients overlap
+    assert bwd(do=DO + 4) == EALIGN
+    assert bwd(ws=None) == EWS and bwd(nb=need - 1) == EWS
+    assert bwd(ws=DG - 512) == EINVAL              # workspace overlaps a gradient
+    assert lib.hybrid_attn_linear_backward(Q, K, V, G, DO, DQ, DK, DV, DG, 1, 2, 0, 64, HA_BF16,
+                                           None, 0, None) == OK

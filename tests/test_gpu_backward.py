@@ -1,0 +1,110 @@
+"""Backward-pass parity: the gradient kernels against the float64 backward
+oracle (which is pinned by finite differences, library autograd and
+invariances) on the same seeded inputs and upstream gradients."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_linear_softmax_amd as ha
+import oracle
+from gpu_util import TOL, rel_err, say
+from workloads import get, layer_inputs_device, layer_inputs_host, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+VARIANTS = [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)]
+
+
+def _inputs(dtype, d, B, H, N, layer=0):
+    base = get("tiny") if dtype == "f32" else get("480p")
+    w = dataclasses.replace(base, d=d)
+    x = layer_inputs_host(w, layer, B=B, H=H, N=N, device=DEV)
+    gen = torch.Generator(device="cpu").manual_seed(1000 + N + d)
+    x["dO"] = torch.randn((B, H, N, d), generator=gen).to(x["Q"].dtype).to(DEV)
+    return x
+
+
+def _linear_term_scales(Q, K, V, G, dO, eps=1e-6):
+    """Sizes of the terms whose difference makes dQ and dK of the linear layer
+    (for one head): dQ = (dn S^T + dden z) [q > 0] and dK = (v dS^T + dz) [k > 0]
+    are each a difference of two terms of comparable size -- exactly zero at
+    N = 1, where the layer is invariant to scaling q or k -- so their rounding
+    error is measured against |dn| |S|^T + |dden| |z| and |v| |dS|^T + |dz|,
+    with |dS| and |dz| the sums of the absolute terms."""
+    fq, fk = np.maximum(Q, 0), np.maximum(K, 0)
+    S, z = fk.T @ V, fk.sum(axis=0)
+    den = fq @ z + eps
+    a = (fq @ S) / den[:, None]
+    s = 1.0 / (1.0 + np.exp(-G))
+    da = dO * s
+    dn = da / den[:, None]
+    dden = -(da * a).sum(axis=1) / den
+    dS_abs, dz_abs = fq.T @ np.abs(dn), fq.T @ np.abs(dden)
+    sq = (np.abs(dn) @ np.abs(S).T + np.abs(dden)[:, None] * np.abs(z)[None, :]) * (Q > 0)
+    sk = (np.abs(V) @ dS_abs.T + dz_abs[None, :]) * (K > 0)
+    return sq, sk
+
+
+def _check(got, ref, tol, label, scales=(None, None, None, None)):
+    worst = 0.0
+    for name, g, r, sc in zip(("dQ", "dK", "dV", "dG"), got, ref, scales):
+        g = to_f64(g)
+        assert np.all(np.isfinite(g)), (label, name)
+        e = rel_err(g, r) if sc is None else float(np.abs(g - r).max() / max(np.abs(sc).max(), 1e-300))
+        worst = max(worst, e)
+        assert e < tol, f"{label} {name}: max rel err {e:.3e} >= {tol}"
+    say(f"  {label}: worst max rel err {worst:.2e}")
+
+
+def _linear_scales_bhnd(Q, K, V, G, dO):
+    sq, sk = (np.empty_like(Q) for _ in range(2))
+    for b in range(Q.shape[0]):
+        for h in range(Q.shape[1]):
+            sq[b, h], sk[b, h] = _linear_term_scales(Q[b, h], K[b, h], V[b, h], G[b, h], dO[b, h])
+    return sq, sk, None, None
+
+
+@pytest.mark.parametrize("dtype,d", VARIANTS)
+@pytest.mark.parametrize("N", [1, 63, 65, 1000, 4099])
+def test_linear_backward_parity(dtype, d, N):
+    B, H = (2, 3) if N <= 1000 else (1, 2)
+    say(f"linear backward {dtype} d={d} B={B} H={H} N={N}")
+    x = _inputs(dtype, d, B, H, N)
+    got = ha.hybrid_attn_linear_backward(x["Q"], x["K"], x["V"], x["G"], x["dO"])
+    torch.cuda.synchronize()
+    inp = [to_f64(x[k]) for k in ("Q", "K", "V", "G", "dO")]
+    ref = oracle.layer_backward("linear", *inp)
+    _check(got, ref, TOL[dtype], f"linear bwd {dtype} d={d} N={N}", _linear_scales_bhnd(*inp))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_linear_backward_deterministic_and_zero(dtype, d):
+    say(f"linear backward determinism {dtype} d={d}")
+    x = _inputs(dtype, d, 1, 2, 3000)
+    a = ha.hybrid_attn_linear_backward(x["Q"], x["K"], x["V"], x["G"], x["dO"])
+    b = ha.hybrid_attn_linear_backward(x["Q"], x["K"], x["V"], x["G"], x["dO"])
+    z = ha.hybrid_attn_linear_backward(x["Q"], x["K"], x["V"], x["G"], torch.zeros_like(x["dO"]))
+    torch.cuda.synchronize()
+    assert all(torch.equal(u, v) for u, v in zip(a, b))
+    assert all(not torch.any(t) for t in z)
+
+
+def test_linear_backward_720p5s_heads():
+    w = get("720p5s")
+    say(f"linear backward 720p5s B={w.B} H={w.H} N={w.N}: generating inputs")
+    x = layer_inputs_device(w, 0, DEV)
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    x["dO"] = torch.randn((w.B, w.H, w.N, w.d), generator=gen, device=DEV).to(x["Q"].dtype)
+    got = ha.hybrid_attn_linear_backward(x["Q"], x["K"], x["V"], x["G"], x["dO"])
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        inp = [to_f64(x[k][b, h]) for k in ("Q", "K", "V", "G", "dO")]
+        ref = oracle.linear_attention_backward(*inp)
+        _check([g[b, h] for g in got], ref, TOL["bf16"], f"720p5s linear bwd head ({b},{h})",
+               (*_linear_term_scales(*inp), None, None))
+    del x, got
+    torch.cuda.empty_cache()
