@@ -25,6 +25,9 @@ __all__ = [
     "hybrid_attn_group",
     "hybrid_attn_group_schedule",
     "hybrid_attn_linear_backward",
+    "hybrid_attn_softmax_lse",
+    "hybrid_attn_softmax_backward",
+    "softmax_backward_workspace_bytes",
     "linear_backward_workspace_bytes",
     "hybrid_attn_proj_in",
     "hybrid_attn_proj_out",
@@ -279,4 +282,44 @@ def hybrid_attn_linear_backward(Q, K, V, G, dO, grads=None, workspace=None, stre
                                                    B, H, N, d, _dtype_code(ref), _ptr(workspace), nbytes,
                                                    _stream(stream)),
            "hybrid_attn_linear_backward")
+    return tuple(grads)
+
+
+def hybrid_attn_softmax_lse(Q, K, V, G, O=None, lse=None, stream=None):
+    """The gated softmax anchor plus the per-row log-sum-exp (float32 [B, H, N]),
+    the forward pass whose outputs hybrid_attn_softmax_backward consumes."""
+    ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
+    B, H, N, d = ref.shape
+    O = torch.empty_like(ref) if O is None else O
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=ref.device) if lse is None else lse
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check(_lib.load().hybrid_attn_softmax_lse(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), _ptr(lse), B, H, N, d,
+                                               _dtype_code(ref), _stream(stream)),
+           "hybrid_attn_softmax_lse")
+    return O, lse
+
+
+def softmax_backward_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.load().hybrid_attn_softmax_backward_workspace_bytes(B, H, N, d, code))
+
+
+def hybrid_attn_softmax_backward(Q, K, V, G, O, dO, lse, grads=None, workspace=None, stream=None):
+    """dQ, dK, dV, dG of the gated softmax anchor; O and lse from
+    hybrid_attn_softmax_lse."""
+    ref = _tensors(("Q", "K", "V", "G", "O", "dO"), (Q, K, V, G, O, dO), 4)
+    B, H, N, d = ref.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    grads = [torch.empty_like(ref) for _ in range(4)] if grads is None else list(grads)
+    _tensors(("dQ", "dK", "dV", "dG"), grads, 4)
+    need = softmax_backward_workspace_bytes(B, H, N, d, ref.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ref.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().hybrid_attn_softmax_backward(*(_ptr(t) for t in (Q, K, V, G, O, dO, lse)),
+                                                    *(_ptr(t) for t in grads), B, H, N, d, _dtype_code(ref),
+                                                    _ptr(workspace), nbytes, _stream(stream)),
+           "hybrid_attn_softmax_backward")
     return tuple(grads)

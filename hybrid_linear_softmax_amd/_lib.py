@@ -33,6 +33,9 @@ SIGNATURES = {
     "hybrid_attn_group_schedule": (_i, [ctypes.POINTER(_i)]),
     "hybrid_attn_linear_backward_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),
     "hybrid_attn_linear_backward": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),
+    "hybrid_attn_softmax_lse": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
+    "hybrid_attn_softmax_backward_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),
+    "hybrid_attn_softmax_backward": (_i, [_p] * 11 + [_i, _i, _i64, _i, _i, _p, _sz, _p]),
     "hybrid_attn_proj_in": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_proj_out": (_i, [_p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_block_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),

@@ -42,6 +42,7 @@ constexpr int kBr = 256;  // queries per block (8 waves x 32)
 constexpr int kBc = 64;   // keys per iteration
 static_assert(kBr == kSparseBlockQ && kBc == kSparseBlockK, "sparse pattern blocks are the tile sizes");
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest unrescaled probability
 
 // LDS column of key k (0..63 inside a key block) in the V^T tile.
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
                                                       int64_t qblocks, int64_t total, float c,
                                                       const int32_t* __restrict__ blk_off,
                                                       const int32_t* __restrict__ blk_idx,
-                                                      int64_t n_idx) {
+                                                      int64_t n_idx, float* __restrict__ lse) {
   constexpr int NT = 512;
   constexpr int KP = D + 8;              // LDS pitch of K rows (elements)
   constexpr int VP = kBc + 8;            // LDS pitch of V^T rows (elements)
@@ -334,6 +335,9 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   const float l = lsum + __shfl_xor(lsum, 32);
   // (sparse) a query block with no valid key has l = 0 and gets O = 0
   const float inv = (SPARSE && !(l > 0.f)) ? 0.f : __builtin_amdgcn_rcpf(l);
+  // natural log of sum_j exp(q . k_j / sqrt(d)) for the backward pass:
+  // l is summed relative to exp2(m c), so lse = (m c + log2 l) ln 2
+  if (lse != nullptr && qrow < N && h == 0) lse[bh * N + qrow] = (m * c + __log2f(l)) * kLn2;
   if (qrow < N) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
                                                   int64_t qblocks, float scale,
                                                   const int32_t* __restrict__ blk_off,
                                                   const int32_t* __restrict__ blk_idx,
-                                                  int64_t n_idx) {
+                                                  int64_t n_idx, float* __restrict__ lse) {
   constexpr int BQ = 64, BK = 32, HD = D / 2;
   __shared__ float sK[BK][D];
   __shared__ float sV[BK][D];
@@ -428,6 +432,7 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
     }
     m = m_new;
   }
+  if (lse != nullptr && qrow < N && half == 0) lse[bh * N + qrow] = m + logf(l);
   if (qrow < N) {
 #pragma unroll
     for (int e = 0; e < HD; ++e) {
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
 
 hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const void* V,
                          const void* G, void* O, int64_t BH, int64_t N, hipStream_t s,
-                         const int32_t* blk_off, const int32_t* blk_idx, int64_t n_idx) {
+                         const int32_t* blk_off, const int32_t* blk_idx, int64_t n_idx, float* lse) {
   if (BH == 0 || N == 0) return hipSuccess;
   const bool sparse = blk_off != nullptr;
   if (bf16) {
@@ -454,7 +459,7 @@ hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const v
     const bf16_t* g = static_cast<const bf16_t*>(G);
     bf16_t* o = static_cast<bf16_t*>(O);
     const dim3 grid(static_cast<unsigned>(total)), block(512);
-    auto go = [&](auto kern) { kern<<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, total, c, blk_off, blk_idx, n_idx); };
+    auto go = [&](auto kern) { kern<<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, total, c, blk_off, blk_idx, n_idx, lse); };
     if (d == 128)
       sparse ? go(anchor_bf16<128, true>) : go(anchor_bf16<128, false>);
     else
@@ -468,7 +473,7 @@ hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const v
     const float* g = static_cast<const float*>(G);
     float* o = static_cast<float*>(O);
     const dim3 grid(static_cast<unsigned>(BH * qb)), block(128);
-    auto go = [&](auto kern) { kern<<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, scale, blk_off, blk_idx, n_idx); };
+    auto go = [&](auto kern) { kern<<<grid, block, 0, s>>>(q, k, v, g, o, N, qb, scale, blk_off, blk_idx, n_idx, lse); };
     if (d == 128)
       sparse ? go(anchor_f32<128, true>) : go(anchor_f32<128, false>);
     else

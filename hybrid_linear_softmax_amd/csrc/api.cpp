@@ -346,6 +346,54 @@ HA_API int hybrid_attn_linear_backward(const void* Q, const void* K, const void*
                                                HA_LINEAR_EPS, workspace, stream));
 }
 
+HA_API int hybrid_attn_softmax_lse(const void* Q, const void* K, const void* V, const void* G, void* O,
+                                   float* lse, int B, int H, int64_t N, int d, ha_dtype dtype,
+                                   hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const void* in[4] = {Q, K, V, G};
+  const size_t in_bytes[4] = {p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes};
+  void* out[2] = {O, lse};
+  const size_t out_bytes[2] = {p.tensor_bytes, static_cast<size_t>(p.BH) * p.N * sizeof(float)};
+  st = check_io(in, in_bytes, 4, out, out_bytes, 2);
+  if (st != HA_OK) return st;
+  return hip_status(ha::launch_anchor(p.bf16, d, Q, K, V, G, O, p.BH, p.N, stream, nullptr, nullptr, 0, lse));
+}
+
+HA_API size_t hybrid_attn_softmax_backward_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype) {
+  Problem p;
+  if (check_shape(B, H, N, d, dtype, &p) != HA_OK || p.BH == 0) return 0;
+  return ha::softmax_bwd_ws(p.BH, p.N, d, p.bf16);
+}
+
+HA_API int hybrid_attn_softmax_backward(const void* Q, const void* K, const void* V, const void* G,
+                                        const void* O, const void* dO, const float* lse, void* dQ, void* dK,
+                                        void* dV, void* dG, int B, int H, int64_t N, int d, ha_dtype dtype,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const size_t tb = p.tensor_bytes, lb = static_cast<size_t>(p.BH) * p.N * sizeof(float);
+  const void* in[7] = {Q, K, V, G, O, dO, lse};
+  const size_t in_bytes[7] = {tb, tb, tb, tb, tb, tb, lb};
+  void* out[4] = {dQ, dK, dV, dG};
+  const size_t out_bytes[4] = {tb, tb, tb, tb};
+  st = check_io(in, in_bytes, 7, out, out_bytes, 4);
+  if (st != HA_OK) return st;
+  const size_t need = ha::softmax_bwd_ws(p.BH, p.N, d, p.bf16);
+  if (workspace == nullptr || workspace_bytes < need) return HA_EWORKSPACE;
+  if (misaligned(workspace)) return HA_EALIGN;
+  for (int i = 0; i < 7; ++i)
+    if (overlaps(workspace, need, in[i], in_bytes[i])) return HA_EINVAL;
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(workspace, need, out[i], out_bytes[i])) return HA_EINVAL;
+  return hip_status(ha::launch_softmax_backward(p.bf16, d, Q, K, V, G, O, dO, lse, dQ, dK, dV, dG, p.BH,
+                                                p.N, workspace, stream));
+}
+
 HA_API int hybrid_attn_proj_in(const void* x, const void* W_in, void* Q, void* K, void* V, void* G,
                                int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream) {
   Problem p;

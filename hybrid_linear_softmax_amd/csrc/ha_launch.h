@@ -51,7 +51,13 @@ constexpr int kSparseBlockK = 64;
 hipError_t launch_anchor(bool bf16, int d, const void* Q, const void* K, const void* V,
                          const void* G, void* O, int64_t BH, int64_t N, hipStream_t s,
                          const int32_t* blk_off = nullptr, const int32_t* blk_idx = nullptr,
-                         int64_t n_idx = 0);
+                         int64_t n_idx = 0, float* lse = nullptr);
+// Backward pass of the anchor given O, dO and the forward's lse (see anchor_bwd.hip).
+size_t softmax_bwd_ws(int64_t BH, int64_t N, int d, bool bf16);
+hipError_t launch_softmax_backward(bool bf16, int d, const void* Q, const void* K, const void* V,
+                                   const void* G, const void* O, const void* dO, const float* lse,
+                                   void* dQ, void* dK, void* dV, void* dG, int64_t BH, int64_t N,
+                                   void* ws, hipStream_t s);
 
 // Workspace of the linear layer's backward pass (byte offsets).
 struct LinearBwdWs {

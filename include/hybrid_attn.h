@@ -175,6 +175,28 @@ HA_API int hybrid_attn_linear_backward(const void* Q, const void* K, const void*
                                        int B, int H, int64_t N, int d, ha_dtype dtype,
                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The gated softmax anchor (as hybrid_attn_softmax) that also writes, per query
+ * row, lse[b, h, i] = ln sum_j exp(q_i . k_j / sqrt(d)) as float32 [B, H, N]:
+ * the forward pass of a training step, whose O and lse the backward consumes.
+ * lse must not overlap O. */
+HA_API int hybrid_attn_softmax_lse(const void* Q, const void* K, const void* V, const void* G, void* O,
+                                   float* lse, int B, int H, int64_t N, int d, ha_dtype dtype,
+                                   hipStream_t stream);
+
+/* Bytes of device workspace hybrid_attn_softmax_backward needs (da and D). */
+HA_API size_t hybrid_attn_softmax_backward_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype);
+
+/* Backward pass of the gated softmax anchor.  O and lse are the outputs of
+ * hybrid_attn_softmax_lse on the same Q, K, V, G.  With s = sigmoid(G),
+ * da = dO s, D_i = dO_i . O_i, P_ij = exp(q_i . k_j / sqrt(d) - lse_i) and
+ * dS_ij = P_ij (da_i . v_j - D_i): dG = dO O (1 - s), dQ = dS K / sqrt(d),
+ * dK = dS^T Q / sqrt(d), dV = P^T da.  Costs about 3.5 forward passes. */
+HA_API int hybrid_attn_softmax_backward(const void* Q, const void* K, const void* V, const void* G,
+                                        const void* O, const void* dO, const float* lse,
+                                        void* dQ, void* dK, void* dV, void* dG,
+                                        int B, int H, int64_t N, int d, ha_dtype dtype,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- Attention block around the group --------------------------------------
  * The hybrid layers sit inside DiT blocks (review page, section 3: the compiled
  * DiT forward; summary page, section 03: the 3:1 interleave).  The block here is

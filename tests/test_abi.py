@@ -196,3 +196,22 @@ def test_linear_backward_errors(lib):
     assert bwd(ws=DG - 512) == EINVAL              # workspace overlaps a gradient
     assert lib.hybrid_attn_linear_backward(Q, K, V, G, DO, DQ, DK, DV, DG, 1, 2, 0, 64, HA_BF16,
                                            None, 0, None) == OK
+
+
+def test_softmax_lse_and_backward_errors(lib):
+    LSE, DQ, DK, DV, DG, DO = (GB * (30 + i) for i in range(6))
+    assert lib.hybrid_attn_softmax_lse(Q, K, V, G, O, None, 1, 2, 100, 64, HA_BF16, None) == EINVAL
+    assert lib.hybrid_attn_softmax_lse(Q, K, V, G, O, LSE + 2, 1, 2, 100, 64, HA_BF16, None) == EALIGN
+    assert lib.hybrid_attn_softmax_lse(Q, K, V, G, O, O + 64, 1, 2, 100, 64, HA_BF16, None) == EINVAL
+    need = lib.hybrid_attn_softmax_backward_workspace_bytes(1, 2, 100, 64, HA_BF16)
+    assert need >= 1 * 2 * 100 * (64 * 2 + 4)
+
+    def bwd(o=O, lse=LSE, dq=DQ, ws=WS, nb=need, d=64):
+        return lib.hybrid_attn_softmax_backward(Q, K, V, G, o, DO, lse, dq, DK, DV, DG, 1, 2, 100, d, HA_BF16,
+                                                ws, nb, None)
+
+    assert bwd(d=96) == EUNSUP
+    assert bwd(lse=None) == EINVAL and bwd(o=None) == EINVAL
+    assert bwd(dq=LSE) == EINVAL                   # a gradient overlaps lse
+    assert bwd(ws=None) == EWS and bwd(nb=need - 1) == EWS
+    assert bwd(ws=LSE - 64) == EINVAL              # workspace overlaps lse

@@ -108,3 +108,119 @@ def test_linear_backward_720p5s_heads():
                (*_linear_term_scales(*inp), None, None))
     del x, got
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- anchor
+
+
+def _softmax_inputs(dtype, d, B, H, N):
+    x = _inputs(dtype, d, B, H, N, layer=3)
+    return x
+
+
+def _softmax_term_scales(Q, K, V, G, dO):
+    """Sizes of the terms behind dQ and dK of the anchor (one head, full N x N):
+    dS = P (dP - D) is a difference of comparable terms -- exactly zero at N = 1,
+    where P = 1 and dP = D -- so the dQ = dS K / sqrt(d) and dK = dS^T Q / sqrt(d)
+    errors are measured against P (|dP| + |D|) |K| / sqrt(d) and its transpose."""
+    d = Q.shape[1]
+    L = Q @ K.T / np.sqrt(d)
+    P = np.exp(L - L.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    s = 1.0 / (1.0 + np.exp(-G))
+    da = dO * s
+    a = P @ V
+    D = (da * a).sum(axis=1)
+    T = P * (np.abs(da @ V.T) + np.abs(D)[:, None])
+    return T @ np.abs(K) / np.sqrt(d), T.T @ np.abs(Q) / np.sqrt(d)
+
+
+def _softmax_scales_bhnd(Q, K, V, G, dO):
+    sq, sk = (np.empty_like(Q) for _ in range(2))
+    for b in range(Q.shape[0]):
+        for h in range(Q.shape[1]):
+            sq[b, h], sk[b, h] = _softmax_term_scales(Q[b, h], K[b, h], V[b, h], G[b, h], dO[b, h])
+    return sq, sk, None, None
+
+
+@pytest.mark.parametrize("dtype,d", VARIANTS)
+@pytest.mark.parametrize("N", [1, 63, 200, 1000, 2051])
+def test_softmax_lse_forward(dtype, d, N):
+    B, H = (1, 2)
+    say(f"softmax lse {dtype} d={d} N={N}")
+    x = _softmax_inputs(dtype, d, B, H, N)
+    O, lse = ha.hybrid_attn_softmax_lse(x["Q"], x["K"], x["V"], x["G"])
+    O2 = ha.hybrid_attn_softmax(x["Q"], x["K"], x["V"], x["G"])
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)                     # the same kernel, one more output
+    for h in range(H):
+        ref = oracle.softmax_lse(to_f64(x["Q"][0, h]), to_f64(x["K"][0, h]))
+        err = np.abs(lse[0, h].cpu().numpy().astype(np.float64) - ref).max()
+        assert err < (5e-3 if dtype == "bf16" else 1e-5), err
+
+
+@pytest.mark.parametrize("dtype,d", VARIANTS)
+@pytest.mark.parametrize("N", [1, 63, 200, 1000, 2051])
+def test_softmax_backward_parity(dtype, d, N):
+    B, H = (2, 2) if N <= 1000 else (1, 2)
+    say(f"softmax backward {dtype} d={d} B={B} H={H} N={N}")
+    x = _softmax_inputs(dtype, d, B, H, N)
+    O, lse = ha.hybrid_attn_softmax_lse(x["Q"], x["K"], x["V"], x["G"])
+    got = ha.hybrid_attn_softmax_backward(x["Q"], x["K"], x["V"], x["G"], O, x["dO"], lse)
+    torch.cuda.synchronize()
+    inp = [to_f64(x[k]) for k in ("Q", "K", "V", "G", "dO")]
+    ref = oracle.layer_backward("softmax", *inp)
+    _check(got, ref, TOL[dtype], f"softmax bwd {dtype} d={d} N={N}", _softmax_scales_bhnd(*inp))
+
+
+def test_softmax_backward_deterministic():
+    x = _softmax_inputs("bf16", 128, 1, 2, 3000)
+    O, lse = ha.hybrid_attn_softmax_lse(x["Q"], x["K"], x["V"], x["G"])
+    a = ha.hybrid_attn_softmax_backward(x["Q"], x["K"], x["V"], x["G"], O, x["dO"], lse)
+    b = ha.hybrid_attn_softmax_backward(x["Q"], x["K"], x["V"], x["G"], O, x["dO"], lse)
+    torch.cuda.synchronize()
+    assert all(torch.equal(u, v) for u, v in zip(a, b))
+
+
+def test_softmax_backward_keys_at_12k():
+    """dK, dV for sampled keys against the oracle's key-sampled form (which
+    normalises every query over all keys) at N = 12,000."""
+    N = 12000
+    say(f"softmax backward sampled keys bf16 N={N}")
+    x = _softmax_inputs("bf16", 128, 1, 1, N)
+    O, lse = ha.hybrid_attn_softmax_lse(x["Q"], x["K"], x["V"], x["G"])
+    dQ, dK, dV, dG = ha.hybrid_attn_softmax_backward(x["Q"], x["K"], x["V"], x["G"], O, x["dO"], lse)
+    torch.cuda.synchronize()
+    keys = np.unique(np.concatenate([np.arange(64), np.arange(N - 70, N),
+                                     np.random.default_rng(4).choice(N, 256, replace=False)]))
+    inp = [to_f64(x[k][0, 0]) for k in ("Q", "K", "V", "G", "dO")]
+    rk, rv = oracle.softmax_attention_backward_keys(*inp, keys)
+    assert rel_err(to_f64(dK[0, 0])[keys], rk) < TOL["bf16"]
+    assert rel_err(to_f64(dV[0, 0])[keys], rv) < TOL["bf16"]
+
+
+def test_softmax_backward_720p5s_sampled():
+    w = get("720p5s")
+    say(f"softmax backward 720p5s B={w.B} H={w.H} N={w.N}: generating inputs")
+    x = layer_inputs_device(w, 3, DEV)
+    gen = torch.Generator(device=DEV).manual_seed(91)
+    x["dO"] = torch.randn((w.B, w.H, w.N, w.d), generator=gen, device=DEV).to(x["Q"].dtype)
+    O, lse = ha.hybrid_attn_softmax_lse(x["Q"], x["K"], x["V"], x["G"])
+    dQ, dK, dV, dG = ha.hybrid_attn_softmax_backward(x["Q"], x["K"], x["V"], x["G"], O, x["dO"], lse)
+    torch.cuda.synchronize()
+    for t in (dQ, dK, dV, dG):
+        assert torch.isfinite(t).all()
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.N - 80, w.N),
+                                     np.random.default_rng(6).choice(w.N, 192, replace=False)]))
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        inp = [to_f64(x[k][b, h]) for k in ("Q", "K", "V", "G", "dO")]
+        rq, rg = oracle.softmax_attention_backward_rows(*inp, rows)
+        eq, eg = rel_err(to_f64(dQ[b, h])[rows], rq), rel_err(to_f64(dG[b, h])[rows], rg)
+        say(f"  720p5s head ({b},{h}) rows {rows.size}: dQ {eq:.2e} dG {eg:.2e}")
+        assert eq < TOL["bf16"] and eg < TOL["bf16"]
+        # a common shift of every key leaves the anchor unchanged: the key
+        # gradients of a head sum to zero (relative to their total size)
+        dk = to_f64(dK[b, h])
+        assert np.abs(dk.sum(axis=0)).max() < 2e-2 * np.abs(dk).sum(axis=0).max()
+    del x, O, lse, dQ, dK, dV, dG
+    torch.cuda.empty_cache()
