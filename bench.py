@@ -17,6 +17,10 @@ kernel over the LVSA frame pattern of the workload's latent grid (a window of
 frames plus periodic global frames), the three linear layers unchanged; the
 extra field then compares against one dense anchor on the same inputs.
 
+--mode train measures one training step of the group: the forward pass (three
+linear layers, the anchor with its log-sum-exp) and the backward pass of all
+four layers for a synthetic upstream gradient, inputs resident in HBM.
+
 --mode block measures the attention block around the group instead: a step is
 hybrid_attn_block on a residual stream x [B, N, H*d] with synthetic weights
 (four sub-layers, each Q/K/V/G projection, the layer, output projection and
@@ -280,6 +284,108 @@ def run_block(args, w):
     print(json.dumps(line), flush=True)
 
 
+def run_train(args, w):
+    import torch
+
+    import hybrid_linear_softmax_amd as ha
+    from workloads import group_inputs_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] train step {w.name}: B={w.B} H={w.H} N={w.N} d={w.d}; generating inputs", file=sys.stderr,
+          flush=True)
+    x = group_inputs_device(w, dev)
+    gen = torch.Generator(device=dev).manual_seed(123)
+    dO4 = torch.randn(x["Q"].shape, generator=gen, device=dev, dtype=torch.float32).to(x["Q"].dtype)
+    O4 = torch.empty_like(x["Q"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    grads = [[torch.empty_like(x["Q"][0]) for _ in range(4)] for _ in range(4)]
+    ws_f = torch.empty(ha.workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(ha.linear_backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(ha.softmax_backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    kinds = ha.hybrid_attn_group_schedule()
+    evs = {}
+
+    def step(timed=False):
+        def mark(name):
+            if timed:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                evs.setdefault(name, []).append(e)
+        mark("start")
+        for l, kind in enumerate(kinds):
+            a = [x[k][l] for k in "QKVG"]
+            if kind == "linear":
+                ha.hybrid_attn_linear(*a, O4[l], workspace=ws_f)
+            else:
+                ha.hybrid_attn_softmax_lse(*a, O4[l], lse)
+        mark("fwd")
+        for l, kind in enumerate(kinds):
+            a = [x[k][l] for k in "QKVG"]
+            if kind == "linear":
+                ha.hybrid_attn_linear_backward(*a, dO4[l], grads=grads[l], workspace=ws_l)
+                mark(f"bwd_linear{l}")
+            else:
+                ha.hybrid_attn_softmax_backward(*a, O4[l], dO4[l], lse, grads=grads[l], workspace=ws_s)
+                mark("bwd_softmax")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} training steps", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step(timed=True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    n = args.steps
+    fwd_ms = sum(evs["start"][i].elapsed_time(evs["fwd"][i]) for i in range(n)) / n
+    prev = "fwd"
+    bwd = {}
+    for l, kind in enumerate(kinds):
+        name = f"bwd_linear{l}" if kind == "linear" else "bwd_softmax"
+        bwd[name] = sum(evs[prev][i].elapsed_time(evs[name][i]) for i in range(n)) / n
+        prev = name
+    BH = w.B * w.H
+    flop = 14.0 * BH * w.N * w.N * w.d      # 7 products of 2 N^2 d: S, dP in each kernel, dQ, dK, dV
+    tf = flop / (bwd["bwd_softmax"] / 1e3) / 1e12
+    roofline = {
+        "kernel": "anchor backward (sm_bwd_dq_bf16 + sm_bwd_dkv_bf16, the step's dominant work)",
+        "bound": "mfma",
+        "achieved": round(tf, 1),
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": None,
+    }
+    lin_bwd_ms = sum(v for k, v in bwd.items() if k.startswith("bwd_linear")) / 3
+    line = {
+        "metric": "hybrid 3:1 group training step (forward + backward) tokens/s",
+        "value": round(w.B * w.N / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_train", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "layers": "linear,linear,linear,softmax", "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "forward_ms": round(fwd_ms, 3),
+        "backward_ms": {k: round(v, 3) for k, v in bwd.items()},
+        "linear_backward_hbm_gbs_min_bytes": round(9 * BH * w.N * w.d * 2 / (lin_bwd_ms / 1e3) / 1e9, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,8 +398,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048, help="softmax rows the oracle baseline samples")
     ap.add_argument("--anchor", choices=("dense", "lvsa"), default="dense",
                     help="dense softmax anchor (default) or the block-sparse LVSA anchor")
-    ap.add_argument("--mode", choices=("group", "block"), default="group",
-                    help="the hybrid group (default) or the attention block around it")
+    ap.add_argument("--mode", choices=("group", "block", "train"), default="group",
+                    help="the hybrid group (default), the attention block around it, or one training "
+                         "step of the group (forward and backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -313,6 +420,8 @@ def main():
         raise SystemExit("bench workloads are the bf16 shapes; the fp32 tiny shape is a test case")
     if args.mode == "block":
         return run_block(args, w)
+    if args.mode == "train":
+        return run_train(args, w)
     sparse = args.anchor == "lvsa"
     label = f"{w.name}_lvsa" if sparse else w.name
     pattern = None
