@@ -217,36 +217,52 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
 }
 
 // ------------------------------------------------------------------ bf16 dK, dV
-// 4 waves x 32 keys per block (K and V rows of the block in LDS for the whole
-// kernel), 64-query steps: S and dP (queries x keys), then dV^T += da^T P and
-// dK^T += Q^T dS.
+// 8 waves: waves w and w + 4 own the same 32 keys (the block's 128 K and V rows
+// sit in LDS for the whole kernel) and take the two 32-query halves of every
+// 64-query step, so each SIMD runs two waves; their dK, dV accumulators are
+// added once at the end.  Per step: S and dP (queries x keys), then
+// dV^T += da^T P and dK^T += Q^T dS.  The next step's Q and da rows are loaded
+// into registers during the current step's MFMAs and written to LDS, row-major
+// and transposed, straight from those registers.
 template <int D>
-__global__ __launch_bounds__(256) void sm_bwd_dkv_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                       const bf16_t* __restrict__ V, const bf16_t* __restrict__ da,
-                                                       const float* __restrict__ lse, const float* __restrict__ Dv,
-                                                       bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int64_t N,
-                                                       int64_t kblocks, int64_t total, float c) {
-  constexpr int NT = 256, BQ = 64, BKW = 128;
+__global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                                          const bf16_t* __restrict__ V, const bf16_t* __restrict__ da,
+                                                          const float* __restrict__ lse, const float* __restrict__ Dv,
+                                                          bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int64_t N,
+                                                          int64_t kblocks, int64_t total, float c) {
+  constexpr int NT = 512, BQ = 64, BKW = 128;
   constexpr int KP = D + 8, TP = BQ + 8, FG = D / 8;
-  constexpr int QCH = BQ * FG / NT;
   constexpr int KCHW = BKW * FG / NT;
   constexpr int KS = D / 16, RB = D / 32;
-  constexpr int TSUB = (BQ / 4) * FG;
-  __shared__ __attribute__((aligned(16))) bf16_t sKw[BKW * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t sVw[BKW * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t sA[BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t sQt[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16_t sAt[D * TP];
-  __shared__ __attribute__((aligned(16))) float sL[BQ];
-  __shared__ __attribute__((aligned(16))) float sD[BQ];
+  constexpr int TSUB = (BQ / 4) * FG;   // 4-query x 8-feature sub-tiles per tensor (<= 256)
+  constexpr int OFF_K = 0;
+  constexpr int OFF_V = OFF_K + BKW * KP * 2;
+  constexpr int OFF_Q = OFF_V + BKW * KP * 2;
+  constexpr int OFF_A = OFF_Q + BQ * KP * 2;
+  constexpr int OFF_QT = OFF_A + BQ * KP * 2;
+  constexpr int OFF_AT = OFF_QT + D * TP * 2;
+  constexpr int OFF_L = OFF_AT + D * TP * 2;
+  constexpr int OFF_D = OFF_L + BQ * 4;
+  constexpr int LDS = OFF_D + BQ * 4;
+  static_assert(4 * RB * 16 * 64 * 4 <= LDS, "the pair reduction reuses the tiles' LDS");
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  bf16_t* sKw = reinterpret_cast<bf16_t*>(lds + OFF_K);
+  bf16_t* sVw = reinterpret_cast<bf16_t*>(lds + OFF_V);
+  bf16_t* sQ = reinterpret_cast<bf16_t*>(lds + OFF_Q);
+  bf16_t* sA = reinterpret_cast<bf16_t*>(lds + OFF_A);
+  bf16_t* sQt = reinterpret_cast<bf16_t*>(lds + OFF_QT);
+  bf16_t* sAt = reinterpret_cast<bf16_t*>(lds + OFF_AT);
+  float* sL = reinterpret_cast<float*>(lds + OFF_L);
+  float* sD = reinterpret_cast<float*>(lds + OFF_D);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
+  const int kw = wave & 3;   // 32-key group
+  const int th = wave >> 2;  // 32-query half of each step
   const int64_t id = xcd_remap(blockIdx.x, total);
   const int64_t bh = id / kblocks;
   const int64_t kbase = (id % kblocks) * BKW;
-  const int64_t krow = kbase + 32 * wave + l32;
+  const int64_t krow = kbase + 32 * kw + l32;
   const int64_t base = bh * N * D;
   const uint32_t head_bytes = static_cast<uint32_t>(N * D * 2);
   const __amdgpu_buffer_rsrc_t rK =
@@ -271,109 +287,134 @@ __global__ __launch_bounds__(256) void sm_bwd_dkv_bf16(const bf16_t* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[rb][r] = 0.f; dv[rb][r] = 0.f; }
 
-  auto transpose_into = [&](const bf16_t* src, bf16_t* dst, int fg, int m) {
-    uint4 r[4];
+  // this thread's sub-tile of the next query step: tensor (Q or da), 4 query
+  // rows 4 m .. 4 m + 3, features 8 fg .. 8 fg + 7
+  const int sub = tid & 255;
+  const bool loader = sub < TSUB;
+  const bool is_a = tid >= 256;
+  const int sfg = sub / (BQ / 4), sm = sub % (BQ / 4);
+  const __amdgpu_buffer_rsrc_t rsrc = is_a ? rA : rQ;
+  bf16_t* dst_row = is_a ? sA : sQ;
+  bf16_t* dst_t = is_a ? sAt : sQt;
+  uint4 pre[4];
+  float preL = 0.f, preD = 0.f;
+  auto fetch = [&](int64_t q0) {
+    if (loader) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const uint4*>(&src[(4 * m + j) * KP + 8 * fg]);
-    const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&r[0]);
-    const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&r[1]);
-    const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&r[2]);
-    const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&r[3]);
-    const int pos = perm16(4 * m);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<uint2*>(&dst[(8 * fg + 2 * p) * TP + pos]) =
-          make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x05040100u), __builtin_amdgcn_perm(r3[p], r2[p], 0x05040100u));
-      *reinterpret_cast<uint2*>(&dst[(8 * fg + 2 * p + 1) * TP + pos]) =
-          make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u), __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
-    }
-  };
-
-  const int64_t nqb = (N + BQ - 1) / BQ;
-  for (int64_t qb = 0; qb < nqb; ++qb) {
-    const int64_t q0 = qb * BQ;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < QCH; ++i) {
-      const int cidx = tid + NT * i;
-      const uint32_t off = static_cast<uint32_t>((q0 + cidx / FG) * (D * 2) + (cidx % FG) * 16);
-      *reinterpret_cast<uint4*>(&sQ[(cidx / FG) * KP + 8 * (cidx % FG)]) = buffer_load16(rQ, off);
-      *reinterpret_cast<uint4*>(&sA[(cidx / FG) * KP + 8 * (cidx % FG)]) = buffer_load16(rA, off);
+      for (int j = 0; j < 4; ++j)
+        pre[j] = buffer_load16(rsrc, static_cast<uint32_t>((q0 + 4 * sm + j) * (D * 2) + sfg * 16));
     }
     if (tid < BQ) {
       const int64_t q = q0 + tid;
       // a query past N contributes nothing: P = exp2(s c - inf) = 0
-      sL[tid] = q < N ? lse[bh * N + q] * kLog2e : INFINITY;
-      sD[tid] = q < N ? Dv[bh * N + q] : 0.f;
+      preL = q < N ? lse[bh * N + q] * kLog2e : INFINITY;
+      preD = q < N ? Dv[bh * N + q] : 0.f;
     }
-    __syncthreads();
-    if (tid < TSUB) {
-      const int fg = tid / (BQ / 4), m = tid % (BQ / 4);
-      transpose_into(sQ, sQt, fg, m);
-      transpose_into(sA, sAt, fg, m);
+  };
+  auto commit = [&]() {
+    if (loader) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&dst_row[(4 * sm + j) * KP + 8 * sfg]) = pre[j];
+      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&pre[0]);
+      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&pre[1]);
+      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&pre[2]);
+      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&pre[3]);
+      const int pos = perm16(4 * sm);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        *reinterpret_cast<uint2*>(&dst_t[(8 * sfg + 2 * p) * TP + pos]) =
+            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x05040100u), __builtin_amdgcn_perm(r3[p], r2[p], 0x05040100u));
+        *reinterpret_cast<uint2*>(&dst_t[(8 * sfg + 2 * p + 1) * TP + pos]) =
+            make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u), __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
+      }
     }
+    if (tid < BQ) {
+      sL[tid] = preL;
+      sD[tid] = preD;
+    }
+  };
+
+  const int64_t nqb = (N + BQ - 1) / BQ;
+  fetch(0);
+  for (int64_t qb = 0; qb < nqb; ++qb) {
+    __syncthreads();   // every wave is done with the previous step's tiles
+    commit();
     __syncthreads();
+    fetch((qb + 1 < nqb ? qb + 1 : qb) * BQ);   // in flight during the MFMAs
+    const int t = th;
+    f32x16 s, dp;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 s, dp;
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+    for (int st = 0; st < KS; ++st) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sQ[(32 * t + l32) * KP + 16 * st + 8 * h]);
+      const bf16x8 aa = *reinterpret_cast<const bf16x8*>(&sA[(32 * t + l32) * KP + 16 * st + 8 * h]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&sKw[(32 * kw + l32) * KP + 16 * st + 8 * h]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&sVw[(32 * kw + l32) * KP + 16 * st + 8 * h]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, dp, 0, 0, 0);
+    }
+    float p[16], ds[16];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sQ[(32 * t + l32) * KP + 16 * st + 8 * h]);
-        const bf16x8 aa = *reinterpret_cast<const bf16x8*>(&sA[(32 * t + l32) * KP + 16 * st + 8 * h]);
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&sKw[(32 * wave + l32) * KP + 16 * st + 8 * h]);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&sVw[(32 * wave + l32) * KP + 16 * st + 8 * h]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, dp, 0, 0, 0);
+    for (int g = 0; g < 4; ++g) {
+      const float4 L4 = *reinterpret_cast<const float4*>(&sL[32 * t + 8 * g + 4 * h]);
+      const float4 D4 = *reinterpret_cast<const float4*>(&sD[32 * t + 8 * g + 4 * h]);
+      const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+      const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -Lr[j]));
+        ds[r] = p[r] * (dp[r] - Dr[j]);
       }
-      float p[16], ds[16];
+    }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 L4 = *reinterpret_cast<const float4*>(&sL[32 * t + 8 * g + 4 * h]);
-        const float4 D4 = *reinterpret_cast<const float4*>(&sD[32 * t + 8 * g + 4 * h]);
-        const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
-        const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+    for (int tt = 0; tt < 2; ++tt) {
+      uint4 pk, dk4;
+      pk.x = pack_bf16(p[8 * tt + 0], p[8 * tt + 1]); pk.y = pack_bf16(p[8 * tt + 2], p[8 * tt + 3]);
+      pk.z = pack_bf16(p[8 * tt + 4], p[8 * tt + 5]); pk.w = pack_bf16(p[8 * tt + 6], p[8 * tt + 7]);
+      dk4.x = pack_bf16(ds[8 * tt + 0], ds[8 * tt + 1]); dk4.y = pack_bf16(ds[8 * tt + 2], ds[8 * tt + 3]);
+      dk4.z = pack_bf16(ds[8 * tt + 4], ds[8 * tt + 5]); dk4.w = pack_bf16(ds[8 * tt + 6], ds[8 * tt + 7]);
+      const bf16x8 pf = as_bf16x8(pk), dsf = as_bf16x8(dk4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g + j;
-          p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -Lr[j]));
-          ds[r] = p[r] * (dp[r] - Dr[j]);
-        }
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        uint4 pk, dk4;
-        pk.x = pack_bf16(p[8 * tt + 0], p[8 * tt + 1]); pk.y = pack_bf16(p[8 * tt + 2], p[8 * tt + 3]);
-        pk.z = pack_bf16(p[8 * tt + 4], p[8 * tt + 5]); pk.w = pack_bf16(p[8 * tt + 6], p[8 * tt + 7]);
-        dk4.x = pack_bf16(ds[8 * tt + 0], ds[8 * tt + 1]); dk4.y = pack_bf16(ds[8 * tt + 2], ds[8 * tt + 3]);
-        dk4.z = pack_bf16(ds[8 * tt + 4], ds[8 * tt + 5]); dk4.w = pack_bf16(ds[8 * tt + 6], ds[8 * tt + 7]);
-        const bf16x8 pf = as_bf16x8(pk), dsf = as_bf16x8(dk4);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const bf16x8 at = *reinterpret_cast<const bf16x8*>(&sAt[(32 * rb + l32) * TP + 32 * t + 16 * tt + 8 * h]);
-          const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&sQt[(32 * rb + l32) * TP + 32 * t + 16 * tt + 8 * h]);
-          dv[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pf, dv[rb], 0, 0, 0);
-          dk[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf, dk[rb], 0, 0, 0);
-        }
+      for (int rb = 0; rb < RB; ++rb) {
+        const bf16x8 at = *reinterpret_cast<const bf16x8*>(&sAt[(32 * rb + l32) * TP + 32 * t + 16 * tt + 8 * h]);
+        const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&sQt[(32 * rb + l32) * TP + 32 * t + 16 * tt + 8 * h]);
+        dv[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pf, dv[rb], 0, 0, 0);
+        dk[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf, dk[rb], 0, 0, 0);
       }
     }
   }
-  if (krow < N) {
-    const float scale = c / kLog2e;
+  // add the two halves' accumulators: waves 4..7 hand theirs to waves 0..3
+  // through LDS (the tiles are no longer needed), dK then dV
+  float* red = reinterpret_cast<float*>(lds);
+  const float scale = c / kLog2e;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+  for (int which = 0; which < 2; ++which) {
+    __syncthreads();
+    if (th == 1)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int f0 = 32 * rb + 8 * g4 + 4 * h;
-        const int64_t off = base + krow * D + f0;
-        *reinterpret_cast<uint2*>(dK + off) =
-            make_uint2(pack_bf16(dk[rb][4 * g4 + 0] * scale, dk[rb][4 * g4 + 1] * scale),
-                       pack_bf16(dk[rb][4 * g4 + 2] * scale, dk[rb][4 * g4 + 3] * scale));
-        *reinterpret_cast<uint2*>(dV + off) =
-            make_uint2(pack_bf16(dv[rb][4 * g4 + 0], dv[rb][4 * g4 + 1]),
-                       pack_bf16(dv[rb][4 * g4 + 2], dv[rb][4 * g4 + 3]));
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((kw * RB + rb) * 16 + r) * 64 + lane] = which == 0 ? dk[rb][r] : dv[rb][r];
+    __syncthreads();
+    if (th == 0 && krow < N) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * g4 + j;
+            const float own = which == 0 ? dk[rb][r] : dv[rb][r];
+            v[j] = (own + red[((kw * RB + rb) * 16 + r) * 64 + lane]) * (which == 0 ? scale : 1.f);
+          }
+          const int f0 = 32 * rb + 8 * g4 + 4 * h;
+          *reinterpret_cast<uint2*>((which == 0 ? dK : dV) + base + krow * D + f0) =
+              make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        }
+    }
   }
 }
 
@@ -524,12 +565,12 @@ hipError_t launch_softmax_backward(bool bf16, int d, const void* Q, const void* 
     if (d == 128) {
       sm_bwd_dq_bf16<128><<<dim3(static_cast<unsigned>(tq)), dim3(256), 0, s>>>(q, k, v, a, lse, Dv,
                                                                                  static_cast<bf16_t*>(dQ), N, qb, tq, c);
-      sm_bwd_dkv_bf16<128><<<dim3(static_cast<unsigned>(tk)), dim3(256), 0, s>>>(
+      sm_bwd_dkv_bf16<128><<<dim3(static_cast<unsigned>(tk)), dim3(512), 0, s>>>(
           q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, tk, c);
     } else {
       sm_bwd_dq_bf16<64><<<dim3(static_cast<unsigned>(tq)), dim3(256), 0, s>>>(q, k, v, a, lse, Dv,
                                                                                 static_cast<bf16_t*>(dQ), N, qb, tq, c);
-      sm_bwd_dkv_bf16<64><<<dim3(static_cast<unsigned>(tk)), dim3(256), 0, s>>>(
+      sm_bwd_dkv_bf16<64><<<dim3(static_cast<unsigned>(tk)), dim3(512), 0, s>>>(
           q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, tk, c);
     }
   } else {
