@@ -17,7 +17,10 @@ from .hybrid_ref import (  # noqa: F401
     layer,
     group,
 )
-from .block_ref import block, merge_heads, project_in, project_out, round_bf16, split_heads  # noqa: F401
+from .block_ref import (  # noqa: F401
+    RMS_EPS, attnres_mix, block, block_routed, merge_heads, project_in, project_out, round_bf16,
+    split_heads, stack_routed,
+)
 from .backward_ref import (  # noqa: F401
     layer_backward,
     linear_attention_backward,

@@ -80,3 +80,61 @@ def block(x, W_in4, W_out4, H, kinds=SCHEDULE, store=None):
         Q, K, V, G = (keep(t) for t in project_in(x, W_in4[l], H))
         x = keep(project_out(keep(layer(kind, Q, K, V, G)), W_out4[l], x))
     return x
+
+
+# ---------------------------------------------------------------------------
+# Block attention residuals (AttnRes).  The pages (summary page, section 03;
+# review page, sections 1 and 3; news item) describe it only in words: instead
+# of a layer reading just the running sum of earlier outputs, summaries of
+# completed blocks are routed into later linear layers.  The reading used here:
+# a block is one hybrid group, its summary is the stream after it, and the
+# projections of each linear sub-layer of a later group read a depth-wise
+# softmax mixture of the completed summaries and the current stream (the stream
+# itself is one candidate, so the plain residual path is kept):
+#     score_b = w . (v_b / rms(v_b)) / sqrt(C),  rms(v) = sqrt(mean(v^2) + eps)
+#     h       = sum_b softmax_b(score) v_b
+# per token, with w a learned routing vector of the sub-layer.  The anchor reads
+# the stream; every residual update still goes to the stream.
+
+RMS_EPS = 1e-6
+
+
+def attnres_mix(candidates, w, eps=RMS_EPS):
+    """h [B, N, C] = softmax-over-candidates mixture of candidates [M, B, N, C]
+    with scores w . rmsnorm(v) / sqrt(C), per token."""
+    V = np.asarray(candidates, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    C = V.shape[-1]
+    rms = np.sqrt((V * V).mean(axis=-1) + eps)                # [M, B, N]
+    score = (V @ w) / rms / np.sqrt(C)                        # [M, B, N]
+    score = score - score.max(axis=0, keepdims=True)
+    a = np.exp(score)
+    a /= a.sum(axis=0, keepdims=True)
+    return (a[..., None] * V).sum(axis=0)
+
+
+def block_routed(x, summaries, w_route, W_in4, W_out4, H, kinds=SCHEDULE, store=None):
+    """One block whose linear sub-layers read attnres_mix(summaries + [stream],
+    w_route[l]); summaries [M, B, N, C] (M may be 0), w_route [L, C]."""
+    x = np.asarray(x, dtype=np.float64)
+    keep = (lambda a: a) if store is None else store
+    summaries = np.asarray(summaries, dtype=np.float64).reshape((-1,) + x.shape)
+    for l, kind in enumerate(kinds):
+        src = x
+        if kind == "linear":
+            src = keep(attnres_mix(np.concatenate([summaries, x[None]], axis=0), w_route[l]))
+        Q, K, V, G = (keep(t) for t in project_in(src, W_in4[l], H))
+        x = keep(project_out(keep(layer(kind, Q, K, V, G)), W_out4[l], x))
+    return x
+
+
+def stack_routed(x, w_route, W_in, W_out, H, store=None):
+    """n blocks in sequence (W_in [n, 4, 4C, C], W_out [n, 4, C, C], w_route
+    [n, 4, C]); block k routes the summaries of blocks 0 .. k-1."""
+    x = np.asarray(x, dtype=np.float64)
+    summaries = []
+    for k in range(len(W_in)):
+        prev = np.stack(summaries) if summaries else np.zeros((0,) + x.shape)
+        x = block_routed(x, prev, w_route[k], W_in[k], W_out[k], H, store=store)
+        summaries.append(x)
+    return x
