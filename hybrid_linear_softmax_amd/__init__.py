@@ -29,6 +29,9 @@ __all__ = [
     "hybrid_attn_softmax_backward",
     "softmax_backward_workspace_bytes",
     "linear_backward_workspace_bytes",
+    "hybrid_attn_attnres_mix",
+    "hybrid_attn_block_routed",
+    "block_routed_workspace_bytes",
     "hybrid_attn_proj_in",
     "hybrid_attn_proj_out",
     "hybrid_attn_block",
@@ -323,3 +326,46 @@ def hybrid_attn_softmax_backward(Q, K, V, G, O, dO, lse, grads=None, workspace=N
                                                     _ptr(workspace), nbytes, _stream(stream)),
            "hybrid_attn_softmax_backward")
     return tuple(grads)
+
+
+def hybrid_attn_attnres_mix(summaries, x, w, h=None, stream=None):
+    """AttnRes mixture h [B, N, C] over the candidates summaries [M, B, N, C]
+    (M may be 0; pass None) and x, with routing vector w (float32 [C])."""
+    B, N, C = _block_dims(x, 1)[:3]
+    M = 0 if summaries is None else summaries.shape[0]
+    if M:
+        if tuple(summaries.shape[1:]) != (B, N, C) or summaries.dtype != x.dtype or not summaries.is_contiguous():
+            raise ValueError("summaries must be a contiguous [M, B, N, C] tensor of x's dtype")
+    if w.dtype != torch.float32 or tuple(w.shape) != (C,) or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 [C] tensor")
+    h = torch.empty_like(x) if h is None else h
+    _check(_lib.load().hybrid_attn_attnres_mix(_ptr(summaries) if M else ctypes.c_void_p(None), M, _ptr(x), _ptr(w),
+                                               _ptr(h), B, N, C, _dtype_code(x), _stream(stream)),
+           "hybrid_attn_attnres_mix")
+    return h
+
+
+def block_routed_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.load().hybrid_attn_block_routed_workspace_bytes(B, H, N, d, code))
+
+
+def hybrid_attn_block_routed(x, summaries, w_route, W_in4, W_out4, heads, x_out=None, workspace=None, stream=None):
+    """hybrid_attn_block with AttnRes routing of `summaries` ([M, B, N, C] or
+    None) into the linear sub-layers; w_route float32 [4, C]."""
+    B, N, C, d = _block_dims(x, heads)
+    _check_weight("W_in4", W_in4, (4, 4 * C, C), x)
+    _check_weight("W_out4", W_out4, (4, C, C), x)
+    if w_route.dtype != torch.float32 or tuple(w_route.shape) != (4, C) or not w_route.is_contiguous():
+        raise ValueError("w_route must be a contiguous float32 [4, C] tensor")
+    M = 0 if summaries is None else summaries.shape[0]
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    need = block_routed_workspace_bytes(B, heads, N, d, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().hybrid_attn_block_routed(_ptr(x), _ptr(summaries) if M else ctypes.c_void_p(None), M,
+                                                _ptr(w_route), _ptr(W_in4), _ptr(W_out4), _ptr(x_out), B, heads, N, d,
+                                                _dtype_code(x), _ptr(workspace), nbytes, _stream(stream)),
+           "hybrid_attn_block_routed")
+    return x_out

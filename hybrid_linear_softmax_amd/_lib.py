@@ -36,6 +36,9 @@ SIGNATURES = {
     "hybrid_attn_softmax_lse": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_softmax_backward_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),
     "hybrid_attn_softmax_backward": (_i, [_p] * 11 + [_i, _i, _i64, _i, _i, _p, _sz, _p]),
+    "hybrid_attn_attnres_mix": (_i, [_p, _i, _p, _p, _p, _i, _i64, _i, _i, _p]),
+    "hybrid_attn_block_routed_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),
+    "hybrid_attn_block_routed": (_i, [_p, _p, _i, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),
     "hybrid_attn_proj_in": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_proj_out": (_i, [_p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_block_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),

@@ -480,6 +480,91 @@ HA_API int hybrid_attn_block(const void* x, const void* W_in4, const void* W_out
   return HA_OK;
 }
 
+HA_API int hybrid_attn_attnres_mix(const void* summaries, int M, const void* x, const float* w, void* h,
+                                   int B, int64_t N, int C, ha_dtype dtype, hipStream_t stream) {
+  if (dtype != HA_BF16 && dtype != HA_F32) return HA_EUNSUPPORTED;
+  if (C <= 0 || C % 8 != 0) return HA_EUNSUPPORTED;
+  if (B < 0 || N < 0 || N > HA_MAX_N || M < 0 || M > HA_ATTNRES_MAX_SUMMARIES) return HA_EINVAL;
+  static_assert(HA_ATTNRES_MAX_SUMMARIES < 64, "candidate scores fit the kernel's table");
+  const int64_t tokens = static_cast<int64_t>(B) * N;
+  if (tokens == 0) return HA_OK;
+  const size_t row_bytes = static_cast<size_t>(tokens) * C * (dtype == HA_BF16 ? 2u : 4u);
+  if (M > 0 && summaries == nullptr) return HA_EINVAL;
+  const void* in[3] = {x, w, M > 0 ? summaries : x};
+  const size_t in_bytes[3] = {row_bytes, static_cast<size_t>(C) * sizeof(float), M * row_bytes};
+  void* out[1] = {h};
+  const size_t out_bytes[1] = {row_bytes};
+  int st = check_io(in, in_bytes, M > 0 ? 3 : 2, out, out_bytes, 1);
+  if (st != HA_OK) return st;
+  return hip_status(ha::launch_attnres_mix(dtype == HA_BF16, summaries, M, x, w, h, tokens, C, HA_RMS_EPS, stream));
+}
+
+HA_API size_t hybrid_attn_block_routed_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype) {
+  Problem p;
+  if (check_shape(B, H, N, d, dtype, &p) != HA_OK || p.BH == 0) return 0;
+  return block_ws(p).total + ((p.tensor_bytes + 255) & ~static_cast<size_t>(255));
+}
+
+HA_API int hybrid_attn_block_routed(const void* x, const void* summaries, int M, const float* w_route,
+                                    const void* W_in4, const void* W_out4, void* x_out, int B, int H, int64_t N,
+                                    int d, ha_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (M < 0 || M > HA_ATTNRES_MAX_SUMMARIES) return HA_EINVAL;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const int64_t C = p.H * p.d;
+  const size_t win_bytes = weight_bytes(p, 4 * C), wout_bytes = weight_bytes(p, C);
+  const bool in_place = x_out == x;
+  if (M > 0 && summaries == nullptr) return HA_EINVAL;
+  const void* in[5] = {W_in4, W_out4, w_route, M > 0 ? summaries : W_in4, x};
+  const size_t in_bytes[5] = {4 * win_bytes, 4 * wout_bytes, static_cast<size_t>(4 * C) * sizeof(float),
+                              M * p.tensor_bytes, p.tensor_bytes};
+  void* out[1] = {x_out};
+  const size_t out_bytes[1] = {p.tensor_bytes};
+  // x may lie inside the summaries (read-only both); x_out may be x itself
+  const int n_in = in_place ? 4 : 5;
+  st = check_io(in, in_bytes, n_in, out, out_bytes, 1);
+  if (st != HA_OK) return st;
+  if (in_place && (x == nullptr || misaligned(x))) return x == nullptr ? HA_EINVAL : HA_EALIGN;
+  const BlockWs L = block_ws(p);
+  const size_t need = L.total + ((p.tensor_bytes + 255) & ~static_cast<size_t>(255));
+  if (workspace == nullptr || workspace_bytes < need) return HA_EWORKSPACE;
+  if (misaligned(workspace)) return HA_EALIGN;
+  for (int i = 0; i < 5; ++i)
+    if ((i < 4 || !in_place) && overlaps(workspace, need, in[i], in_bytes[i])) return HA_EINVAL;
+  if (overlaps(workspace, need, x_out, p.tensor_bytes)) return HA_EINVAL;
+
+  char* w = static_cast<char*>(workspace);
+  void *q = w + L.q, *k = w + L.k, *v = w + L.v, *g = w + L.g, *o = w + L.o, *lin = w + L.lin;
+  void* hbuf = w + L.total;
+  int kinds[4];
+  hybrid_attn_group_schedule(kinds);
+  for (int l = 0; l < 4; ++l) {
+    const void* xin = l == 0 ? x : x_out;
+    const char* wi = static_cast<const char*>(W_in4) + static_cast<size_t>(l) * win_bytes;
+    const char* wo = static_cast<const char*>(W_out4) + static_cast<size_t>(l) * wout_bytes;
+    const void* src = xin;
+    if (kinds[l] == 0) {
+      st = hip_status(ha::launch_attnres_mix(p.bf16, summaries, M, xin, w_route + l * C, hbuf, p.B * p.N,
+                                             static_cast<int>(C), HA_RMS_EPS, stream));
+      if (st != HA_OK) return st;
+      src = hbuf;
+    }
+    st = hip_status(ha::launch_proj_in(p.bf16, src, wi, q, k, v, g, p.B, p.H, p.N, d, stream));
+    if (st != HA_OK) return st;
+    if (kinds[l] == 0)
+      st = run_linear(p, q, k, v, g, o, lin, stream);
+    else
+      st = hip_status(ha::launch_anchor(p.bf16, d, q, k, v, g, o, p.BH, p.N, stream));
+    if (st != HA_OK) return st;
+    st = hip_status(ha::launch_proj_out(p.bf16, o, wo, xin, x_out, p.B, p.H, p.N, d, stream));
+    if (st != HA_OK) return st;
+  }
+  return HA_OK;
+}
+
 HA_API int hybrid_attn_group_schedule(int kinds[4]) {
   if (kinds == nullptr) return HA_EINVAL;
   static const int schedule[4] = {0, 0, 0, 1};

@@ -1,0 +1,122 @@
+// Block attention residuals (AttnRes; SANA-Video 2.0 summary page, section 03;
+// review page, sections 1 and 3; news item): summaries of completed blocks are
+// routed into later linear layers.  Per token, the input of such a layer is a
+// softmax mixture over candidates v_0 .. v_{M} (the completed summaries, then
+// the current stream):
+//   score_m = w . v_m / rms(v_m) / sqrt(C),  rms(v) = sqrt(mean(v^2) + eps),
+//   h = sum_m softmax_m(score) v_m.
+// HBM-bound: one wave per token reads every candidate row once for the scores
+// (w . v and v . v, reduced over the wave), then again -- from L2, the rows were
+// just read -- for the weighted sum.
+#include <type_traits>
+
+#include "ha_device.h"
+#include "ha_launch.h"
+
+namespace ha {
+
+namespace {
+
+constexpr int kMaxCand = 64;
+
+template <typename T>
+__device__ __forceinline__ void ld8(const T* p, float (&v)[8]) {
+  if constexpr (std::is_same<T, float>::value) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+    v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void st8(T* p, const float (&v)[8]) {
+  if constexpr (std::is_same<T, float>::value) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
+                                              pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7]));
+  }
+}
+
+// candidate m of token t: summaries[m] for m < M, x for m == M
+template <typename T>
+__global__ __launch_bounds__(256) void attnres_mix_kernel(const T* __restrict__ summaries, int M,
+                                                          const T* __restrict__ x, const float* __restrict__ w,
+                                                          T* __restrict__ h, int64_t tokens, int C, float eps) {
+  __shared__ float sScore[4][kMaxCand];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tok = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (tok >= tokens) return;   // a whole wave: no barrier below
+  const int nch = C / 8;
+  auto row = [&](int m) -> const T* {
+    return (m < M ? summaries + static_cast<int64_t>(m) * tokens * C : x) + tok * C;
+  };
+  const float inv_c = 1.0f / static_cast<float>(C);
+  const float inv_sqrt_c = rsqrtf(static_cast<float>(C));
+  float mx = -INFINITY;
+  for (int m = 0; m <= M; ++m) {
+    const T* v = row(m);
+    float dot = 0.f, ss = 0.f;
+    for (int ch = lane; ch < nch; ch += 64) {
+      float a[8];
+      ld8(v + 8 * ch, a);
+      const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * ch);
+      const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * ch + 4);
+      dot = fmaf(a[0], w0.x, dot); dot = fmaf(a[1], w0.y, dot);
+      dot = fmaf(a[2], w0.z, dot); dot = fmaf(a[3], w0.w, dot);
+      dot = fmaf(a[4], w1.x, dot); dot = fmaf(a[5], w1.y, dot);
+      dot = fmaf(a[6], w1.z, dot); dot = fmaf(a[7], w1.w, dot);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss = fmaf(a[k], a[k], ss);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      dot += __shfl_xor(dot, o);
+      ss += __shfl_xor(ss, o);
+    }
+    const float sc = dot * rsqrtf(ss * inv_c + eps) * inv_sqrt_c;
+    mx = fmaxf(mx, sc);
+    if (lane == 0) sScore[wave][m] = sc;
+  }
+  __builtin_amdgcn_wave_barrier();
+  float den = 0.f;
+  for (int m = 0; m <= M; ++m) den += __expf(sScore[wave][m] - mx);
+  const float inv = 1.0f / den;
+  for (int ch = lane; ch < nch; ch += 64) {
+    float acc[8] = {};
+    for (int m = 0; m <= M; ++m) {
+      const float a_m = __expf(sScore[wave][m] - mx) * inv;
+      float v[8];
+      ld8(row(m) + 8 * ch, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = fmaf(a_m, v[k], acc[k]);
+    }
+    st8(h + tok * C + 8 * ch, acc);
+  }
+}
+
+}  // namespace
+
+int attnres_max_candidates() { return kMaxCand; }
+
+hipError_t launch_attnres_mix(bool bf16, const void* summaries, int M, const void* x, const float* w, void* h,
+                              int64_t tokens, int C, float eps, hipStream_t s) {
+  if (tokens == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((tokens + 3) / 4)), block(256);
+  if (bf16)
+    attnres_mix_kernel<bf16_t><<<grid, block, 0, s>>>(static_cast<const bf16_t*>(summaries), M,
+                                                      static_cast<const bf16_t*>(x), w, static_cast<bf16_t*>(h),
+                                                      tokens, C, eps);
+  else
+    attnres_mix_kernel<float><<<grid, block, 0, s>>>(static_cast<const float*>(summaries), M,
+                                                     static_cast<const float*>(x), w, static_cast<float*>(h),
+                                                     tokens, C, eps);
+  return hipGetLastError();
+}
+
+}  // namespace ha

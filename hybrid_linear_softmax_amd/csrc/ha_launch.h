@@ -75,6 +75,11 @@ hipError_t launch_linear_backward(bool bf16, int d, const void* Q, const void* K
                                   const void* G, const void* dO, void* dQ, void* dK, void* dV, void* dG,
                                   int64_t BH, int64_t N, float eps, void* ws, hipStream_t s);
 
+// AttnRes mixture over candidates summaries[0 .. M-1] then x (each [tokens, C]).
+int attnres_max_candidates();
+hipError_t launch_attnres_mix(bool bf16, const void* summaries, int M, const void* x, const float* w, void* h,
+                              int64_t tokens, int C, float eps, hipStream_t s);
+
 // Block projections: Q, K, V, G = split_heads(x W_in^T) and
 // x_out = x + concat_heads(O) W_out^T (x_out may be x).
 hipError_t launch_proj_in(bool bf16, const void* x, const void* W_in, void* Q, void* K, void* V, void* G,

@@ -237,6 +237,41 @@ HA_API int hybrid_attn_block(const void* x, const void* W_in4, const void* W_out
                              int B, int H, int64_t N, int d, ha_dtype dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Block attention residuals (AttnRes) ------------------------------------
+ * Summaries of completed blocks are routed into later linear layers (summary
+ * page, section 03; review page, sections 1 and 3; news item).  The pages give
+ * no formula; the reading implemented here: a block is one hybrid group, its
+ * summary is the stream after it, and each linear sub-layer of a later block
+ * projects, instead of the stream x, the per-token softmax mixture
+ *     h = sum_m softmax_m(w . v_m / rms(v_m) / sqrt(C)) v_m,
+ *     rms(v) = sqrt(mean(v^2) + HA_RMS_EPS),
+ * over the candidates v_0 .. v_{M-1} = the completed summaries and v_M = x,
+ * with w a learned float32 routing vector of the sub-layer.  The anchor reads
+ * x; every residual update still goes to x. */
+#define HA_RMS_EPS 1e-6f
+#define HA_ATTNRES_MAX_SUMMARIES 63
+
+/* h = the mixture above.  summaries: M stacked [B, N, C] arrays (M in
+ * [0, HA_ATTNRES_MAX_SUMMARIES]; may be NULL when M = 0), x, h: [B, N, C],
+ * w: float32 [C].  h must not overlap any input. */
+HA_API int hybrid_attn_attnres_mix(const void* summaries, int M, const void* x, const float* w, void* h,
+                                   int B, int64_t N, int C, ha_dtype dtype, hipStream_t stream);
+
+/* Bytes of device workspace hybrid_attn_block_routed needs: the block's and
+ * one [B, N, C] mixture. */
+HA_API size_t hybrid_attn_block_routed_workspace_bytes(int B, int H, int64_t N, int d, ha_dtype dtype);
+
+/* hybrid_attn_block with AttnRes: sub-layer l, when linear, projects
+ * hybrid_attn_attnres_mix(summaries, M, stream, w_route + l * C) instead of the
+ * stream.  w_route: float32 [4, C] (the anchor's row is unused).  x_out may be
+ * x; it must not overlap the summaries, so a stack of blocks can write block
+ * k's output straight into slot k of its summaries array and pass slots
+ * 0 .. k-1 as the next block's summaries. */
+HA_API int hybrid_attn_block_routed(const void* x, const void* summaries, int M, const float* w_route,
+                                    const void* W_in4, const void* W_out4, void* x_out,
+                                    int B, int H, int64_t N, int d, ha_dtype dtype,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Writes the layer kinds of a group in order: 0 = gated linear, 1 = gated
  * softmax anchor; i.e. {0, 0, 0, 1}.  Returns HA_EINVAL for a NULL array. */
 HA_API int hybrid_attn_group_schedule(int kinds[4]);

@@ -215,3 +215,27 @@ def test_softmax_lse_and_backward_errors(lib):
     assert bwd(dq=LSE) == EINVAL                   # a gradient overlaps lse
     assert bwd(ws=None) == EWS and bwd(nb=need - 1) == EWS
     assert bwd(ws=LSE - 64) == EINVAL              # workspace overlaps lse
+
+
+def test_attnres_errors(lib):
+    X, Hh, W, SUM = GB * 40, GB * 41, GB * 42, GB * 43
+    mix = lib.hybrid_attn_attnres_mix
+    assert mix(SUM, 2, X, W, Hh, 1, 100, 100, HA_BF16, None) == EUNSUP      # C not a multiple of 8
+    assert mix(SUM, 2, X, W, Hh, 1, 100, 128, 9, None) == EUNSUP
+    assert mix(SUM, 64, X, W, Hh, 1, 100, 128, HA_BF16, None) == EINVAL     # too many summaries
+    assert mix(None, 2, X, W, Hh, 1, 100, 128, HA_BF16, None) == EINVAL
+    assert mix(SUM, 2, X, W + 4, Hh, 1, 100, 128, HA_BF16, None) == EALIGN
+    assert mix(SUM, 2, X, W, X + 256, 1, 100, 128, HA_BF16, None) == EINVAL  # h overlaps x
+    assert mix(SUM, 2, X, W, SUM + 256, 1, 100, 128, HA_BF16, None) == EINVAL
+    assert mix(None, 0, X, W, Hh, 1, 0, 128, HA_BF16, None) == OK
+    need = lib.hybrid_attn_block_routed_workspace_bytes(1, 2, 100, 64, HA_BF16)
+    assert need > lib.hybrid_attn_block_workspace_bytes(1, 2, 100, 64, HA_BF16)
+    tb = 100 * 128 * 2
+
+    def blk(x=X, s=SUM, m=2, xo=Hh, ws=WS, nb=need):
+        return lib.hybrid_attn_block_routed(x, s, m, W, Q, K, xo, 1, 2, 100, 64, HA_BF16, ws, nb, None)
+
+    assert blk(m=64) == EINVAL and blk(s=None) == EINVAL
+    assert blk(xo=SUM + tb) == EINVAL               # output inside the summaries
+    assert blk(ws=None) == EWS and blk(nb=need - 1) == EWS
+    assert blk(ws=SUM - 512) == EINVAL
