@@ -21,6 +21,10 @@ extra field then compares against one dense anchor on the same inputs.
 linear layers, the anchor with its log-sum-exp) and the backward pass of all
 four layers for a synthetic upstream gradient, inputs resident in HBM.
 
+--mode stack measures --blocks attention blocks with block attention residuals
+(AttnRes): the linear sub-layers of block k project a per-token softmax mixture
+of the outputs of blocks 0 .. k-1 and the current stream.
+
 --mode block measures the attention block around the group instead: a step is
 hybrid_attn_block on a residual stream x [B, N, H*d] with synthetic weights
 (four sub-layers, each Q/K/V/G projection, the layer, output projection and
@@ -386,6 +390,94 @@ def run_train(args, w):
     print(json.dumps(line), flush=True)
 
 
+def run_stack(args, w):
+    import dataclasses
+
+    import torch
+
+    import hybrid_linear_softmax_amd as ha
+    from workloads import block_inputs_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    C = w.H * w.d
+    M = w.B * w.N
+    nb = args.blocks
+    print(f"[bench] AttnRes stack {w.name}: {nb} blocks, B={w.B} N={w.N} C={C}; generating inputs",
+          file=sys.stderr, flush=True)
+    ins = [block_inputs_device(dataclasses.replace(w, seed=k), dev) for k in range(nb)]
+    x = ins[0]["x"]
+    W_in = [t["W_in"] for t in ins]
+    W_out = [t["W_out"] for t in ins]
+    for t in ins[1:]:
+        del t["x"]
+    gen = torch.Generator(device=dev).manual_seed(5)
+    w_route = torch.randn((nb, 4, C), generator=gen, device=dev, dtype=torch.float32)
+    summaries = torch.empty((nb, w.B, w.N, C), dtype=x.dtype, device=dev)
+    ws = torch.empty(ha.block_routed_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for k in range(nb):
+            ha.hybrid_attn_block_routed(x if k == 0 else summaries[k - 1], summaries[:k] if k else None,
+                                        w_route[k], W_in[k], W_out[k], w.H, x_out=summaries[k], workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} stack steps", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    # the routing alone, as block nb-1 runs it (nb - 1 summaries + the stream)
+    h = torch.empty_like(x)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    S = summaries[:nb - 1] if nb > 1 else None
+    ha.hybrid_attn_attnres_mix(S, summaries[nb - 1], w_route[0, 0], h)
+    e0.record()
+    for _ in range(5):
+        ha.hybrid_attn_attnres_mix(S, summaries[nb - 1], w_route[0, 0], h)
+    e1.record()
+    torch.cuda.synchronize()
+    mix_ms = e0.elapsed_time(e1) / 5
+    mix_bytes = (nb + 1) * M * C * 2   # nb candidates read once, h written
+    line = {
+        "metric": "stack of AttnRes-routed attention blocks tokens/s",
+        "value": round(M / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_attnres_stack", "blocks": nb, "B": w.B, "N": w.N, "H": w.H, "d": w.d,
+                   "parallelism": "single-gpu"},
+        "roofline": {
+            "kernel": f"attnres_mix_kernel ({nb} candidates)",
+            "bound": "hbm",
+            "achieved": round(mix_bytes / (mix_ms / 1e3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(mix_bytes / (mix_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+        "block_ms": round(ms_per_step / nb, 3),
+        "mix_ms": round(mix_ms, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,9 +490,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048, help="softmax rows the oracle baseline samples")
     ap.add_argument("--anchor", choices=("dense", "lvsa"), default="dense",
                     help="dense softmax anchor (default) or the block-sparse LVSA anchor")
-    ap.add_argument("--mode", choices=("group", "block", "train"), default="group",
-                    help="the hybrid group (default), the attention block around it, or one training "
-                         "step of the group (forward and backward)")
+    ap.add_argument("--mode", choices=("group", "block", "train", "stack"), default="group",
+                    help="the hybrid group (default), the attention block around it, one training "
+                         "step of the group (forward and backward), or a stack of AttnRes-routed blocks")
+    ap.add_argument("--blocks", type=int, default=4, help="blocks in --mode stack")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -422,6 +515,8 @@ def main():
         return run_block(args, w)
     if args.mode == "train":
         return run_train(args, w)
+    if args.mode == "stack":
+        return run_stack(args, w)
     sparse = args.anchor == "lvsa"
     label = f"{w.name}_lvsa" if sparse else w.name
     pattern = None
