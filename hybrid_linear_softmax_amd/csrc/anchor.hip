@@ -19,10 +19,11 @@
 //    stores of a wave fall on distinct LDS banks;
 //  * K and V are read with buffer loads whose record count is the head's size:
 //    rows past N read as zero without any per-load bounds arithmetic;
-//  * software pipeline: the logit MFMAs of key block j+1 are issued while the
-//    softmax of block j runs on the VALU (same wave); K and V tiles are double-
+//  * software pipeline: the logit MFMAs of key block j+1 are interleaved, in
+//    one wave's instruction stream, with the softmax of block j, and the PV
+//    MFMAs of block j with the row max of block j+1; K and V tiles are double-
 //    buffered in LDS, K one block ahead of V, one barrier per key block, and
-//    the loads of the next tiles are in flight during the MFMAs;
+//    the global loads of the next tiles are issued at the top of the step;
 //  * the running maximum is updated lazily: the output is rescaled only when a
 //    row maximum grows by more than 2^8 in exp2 units (the probabilities stay
 //    below 256, exact enough in fp32 and bf16), which after the first blocks is
@@ -187,37 +188,6 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     }
   };
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  auto softmax_p = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2]) {
-    // (sparse) while every key seen so far was masked, m = -inf: keep p = 0
-    const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[t][8 * tt + j], c, -mc));
-        uint4 pk;
-        pk.x = pack_bf16(p[0], p[1]); pk.y = pack_bf16(p[2], p[3]);
-        pk.z = pack_bf16(p[4], p[5]); pk.w = pack_bf16(p[6], p[7]);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.x), one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.y), one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.z), one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.w), one, lsum, false);
-        pf[t][tt] = as_bf16x8(pk);
-      }
-  };
-  auto pv = [&](int b, const bf16x8 (&pf)[2][2]) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sVt[b][(32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h]);
-          o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][tt], o[rb], 0, 0, 0);
-        }
-  };
   // K and V use separate double buffers; K runs one block ahead of V:
   // step j reads K_{j+1} (buffer (j+1)&1) and V_j (buffer j&1) and stores
   // K_{j+2} into K buffer j&1 and V_{j+1} into V buffer (j+1)&1.
@@ -287,19 +257,85 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   __syncthreads();
   // step j: k1, k2 are the first keys of blocks j+1 and j+2; masked steps
   // apply the key limit lim1 of block j+1 (in sparse mode only when it is
-  // below 64: the branch sits after the PV MFMAs, off the softmax-PV chain)
+  // below 64).  The step is written in the order it should issue: each logit
+  // MFMA of block j+1 is followed by two probabilities of block j (exp2, bf16
+  // pack, row-sum dot), each PV MFMA of block j by a slice of block j+1's row
+  // max, K/V fragments read two MFMAs ahead.  Empty asm statements that consume
+  // each slice's result pin it between its MFMAs: left alone, the compiler
+  // sinks the VALU work to its first use and clusters the MFMAs.
   auto step = [&](int64_t j, int64_t k1, int64_t k2, int lim1, f32x16 (&scur)[2], f32x16 (&snext)[2],
                   auto masked) {
+    const int kb = static_cast<int>((j + 1) & 1);
+    const int vb = static_cast<int>(j & 1);
     load_k(k2);
+    load_v(k1);
+    // (sparse) while every key seen so far was masked, m = -inf: keep p = 0
+    const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
+    auto kfrag = [&](int i) -> bf16x8 {
+      const int t = i & 1, st = i >> 1;
+      return *reinterpret_cast<const bf16x8*>(&sK[kb][(32 * t + l32) * KP + 16 * st + 8 * h]);
+    };
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) snext[t][r] = 0.f;
+    constexpr int NQK = 2 * KS;          // logit MFMAs per block
+    constexpr int PER = 16 / NQK;        // probability pairs per logit MFMA
+    static_assert(PER * NQK == 16, "16 probability pairs per lane and block");
+    bf16x8 kf[2] = {kfrag(0), kfrag(1)};
+    uint32_t pk[16];
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int t = i & 1, st = i >> 1;
+      const bf16x8 a = kf[i & 1];
+      if (i + 2 < NQK) kf[i & 1] = kfrag(i + 2);
+      snext[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], snext[t], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int pi = i * PER + u, e0 = 2 * pi, e1 = e0 + 1;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[e0 >> 4][e0 & 15], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[e1 >> 4][e1 & 15], c, -mc));
+        pk[pi] = pack_bf16(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[pi]), one, lsum, false);
+        asm volatile("" : "+v"(pk[pi]), "+v"(lsum));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P^T operands: pf[t][tt] holds keys 32 t + 16 tt + (the accumulator's 8)
     bf16x8 pf[2][2];
-    qk(static_cast<int>((j + 1) & 1), snext);
-    softmax_p(scur, pf);
-    load_v(k1);  // V is stored at the end of the step: short live range
-    pv(static_cast<int>(j & 1), pf);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        pf[t][tt] = as_bf16x8(make_uint4(pk[8 * t + 4 * tt], pk[8 * t + 4 * tt + 1], pk[8 * t + 4 * tt + 2],
+                                         pk[8 * t + 4 * tt + 3]));
     if (decltype(masked)::value) {
       if (!SPARSE || lim1 < kBc) mask(snext, lim1);
     }
-    const float mx = rowmax(snext);
+    auto vfrag = [&](int i) -> bf16x8 {
+      const int rb = i % RB, q = i / RB, t = q >> 1, tt = q & 1;
+      return *reinterpret_cast<const bf16x8*>(&sVt[vb][(32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h]);
+    };
+    constexpr int NPV = 4 * RB;          // PV MFMAs per block
+    constexpr int PERM = 32 / NPV;       // logits of the row max per PV MFMA
+    static_assert(PERM * NPV == 32 && PERM % 2 == 0, "32 logits per lane and block");
+    bf16x8 vf[2] = {vfrag(0), vfrag(1)};
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int rb = i % RB, q = i / RB, t = q >> 1, tt = q & 1;
+      const bf16x8 a = vf[i & 1];
+      if (i + 2 < NPV) vf[i & 1] = vfrag(i + 2);
+      o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t][tt], o[rb], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < PERM; u += 2) {
+        const int e0 = i * PERM + u, e1 = e0 + 1;
+        mx = fmaxf(mx, fmaxf(snext[e0 >> 4][e0 & 15], snext[e1 >> 4][e1 & 15]));
+      }
+      asm volatile("" : "+v"(mx));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
     store_kv(static_cast<int>(j & 1), static_cast<int>((j + 1) & 1));
     rescale(mx);
     __syncthreads();
