@@ -78,12 +78,12 @@ def measured_traffic(label: str):
         return None
 
 
-def cpu_baseline(w, x, rows_sampled: int, pattern=None):
+def cpu_baseline(w, x, rows_sampled: int, pattern=None, lin_heads: int = 4):
     """The oracle as it stands, timed on this host on a sample of the workload:
-    the full linear layer of one (b, h) head, and `rows_sampled` query rows of
-    the softmax anchor of one head (rows are independent, each costs the same),
-    extrapolated to one whole group.  With a block-sparse pattern the rows are
-    whole query blocks and the extrapolation is by query-key pairs."""
+    the full linear layer of `lin_heads` (b, h) heads, and `rows_sampled` query
+    rows of the softmax anchor of one head (rows are independent, each costs the
+    same), extrapolated to one whole group.  With a block-sparse pattern the rows
+    are whole query blocks and the extrapolation is by query-key pairs."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -92,10 +92,14 @@ def cpu_baseline(w, x, rows_sampled: int, pattern=None):
 
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"],
                   default=1)
-    q, k, v, g = (to_f64(x[n][0, 0, 0]) for n in "QKVG")
-    t0 = time.perf_counter()
-    oracle.linear_attention(q, k, v, g)
-    t_lin = time.perf_counter() - t0
+    lin_heads = max(1, min(lin_heads, w.H))
+    t_lin = 0.0
+    for hh in range(lin_heads):
+        q, k, v, g = (to_f64(x[n][0, 0, hh]) for n in "QKVG")
+        t0 = time.perf_counter()
+        oracle.linear_attention(q, k, v, g)
+        t_lin += time.perf_counter() - t0
+    t_lin /= lin_heads
     q, k, v, g = (to_f64(x[n][3, 0, 0]) for n in "QKVG")
     if pattern is None:
         rows = np.random.default_rng(0).choice(w.N, size=min(rows_sampled, w.N), replace=False)
@@ -121,7 +125,8 @@ def cpu_baseline(w, x, rows_sampled: int, pattern=None):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle: full linear layer of 1 of {heads} heads ({t_lin:.2f} s) and "
+        "sample": (f"float64 numpy oracle: full linear layer of {lin_heads} of {heads} heads "
+                   f"({t_lin:.2f} s each) and "
                    f"{rows.size} of {w.N} {'block-sparse ' if pattern else ''}softmax query rows of 1 head "
                    f"({t_rows:.2f} s), extrapolated "
                    f"to 3 linear + 1 softmax layers over {heads} heads ({t_group:.0f} s per group)"),
@@ -264,7 +269,7 @@ def run_block(args, w):
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = block_cpu_baseline(w, blk, args.cpu_rows)
+        cpu = block_cpu_baseline(w, blk, args.cpu_rows or 2048)
     line = {
         "metric": "attention block (4 projected sub-layers around the 3:1 group) tokens/s",
         "value": round(M / (ms_per_step / 1e3), 1),
@@ -487,7 +492,9 @@ def main():
     ap.add_argument("--allsoftmax-steps", type=int, default=3,
                     help="steps of the all-softmax group (4 anchors) for the speedup ratio; 0 skips")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="softmax rows the oracle baseline samples")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="softmax rows the oracle baseline samples (default: 32768 for the group, about 10 s "
+                         "of host work; 2048 for --mode block)")
     ap.add_argument("--anchor", choices=("dense", "lvsa"), default="dense",
                     help="dense softmax anchor (default) or the block-sparse LVSA anchor")
     ap.add_argument("--mode", choices=("group", "block", "train", "stack"), default="group",
@@ -640,7 +647,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x, args.cpu_rows, pattern)
+        cpu = cpu_baseline(w, x, args.cpu_rows or 32768, pattern)
 
     line = {
         "metric": ("hybrid 3:1 attention group (block-sparse LVSA anchor) tokens/s; % of bf16 MFMA peak"
