@@ -169,6 +169,8 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
       }
     }
     __syncthreads();
+    // valid keys of this block, less this lane's accumulator row offset 4 h
+    const int limh = static_cast<int>(min((int64_t)BK, N - k0)) - 4 * h;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16 s, dp;
@@ -184,8 +186,7 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float p = key < N ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2)) : 0.f;
+        const float p = 32 * t + 8 * (r >> 2) + (r & 3) < limh ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2)) : 0.f;
         ds[r] = p * (dp[r] - Dq);
       }
 #pragma unroll
