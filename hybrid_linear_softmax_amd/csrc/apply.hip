@@ -74,8 +74,8 @@ __global__ __launch_bounds__(256) void apply_bf16(const bf16_t* __restrict__ Q,
       qv[i] = make_uint4(0, 0, 0, 0);
       gv[i] = make_uint4(0, 0, 0, 0);
       if (t < te && tok < N) {
-        qv[i] = *reinterpret_cast<const uint4*>(Q + base + tok * D + 8 * fg);
-        gv[i] = *reinterpret_cast<const uint4*>(G + base + tok * D + 8 * fg);
+        qv[i] = load_stream(Q + base + tok * D + 8 * fg);
+        gv[i] = load_stream(G + base + tok * D + 8 * fg);
       }
     }
   };
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void apply_bf16(const bf16_t* __restrict__ Q,
         o.y = pack_bf16(gate_fast(bf_lo(g.y)) * n0.z * inv, gate_fast(bf_hi(g.y)) * n0.w * inv);
         o.z = pack_bf16(gate_fast(bf_lo(g.z)) * n1.x * inv, gate_fast(bf_hi(g.z)) * n1.y * inv);
         o.w = pack_bf16(gate_fast(bf_lo(g.w)) * n1.z * inv, gate_fast(bf_hi(g.w)) * n1.w * inv);
-        *reinterpret_cast<uint4*>(O + base + tok * D + 8 * fg) = o;
+        store_stream(O + base + tok * D + 8 * fg, o);
       }
     }
     __syncthreads();

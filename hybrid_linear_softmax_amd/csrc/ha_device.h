@@ -13,6 +13,21 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte accesses for data a kernel touches exactly once (the apply
+// kernel's Q, G and O): non-temporal loads and stores.  On this part a
+// read-two-write-one stream runs ~10 % faster this way; a read-only stream
+// (the KV-state reduction) runs slower, so it keeps plain loads.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
 
 // phi = ReLU on two bf16 packed in a dword: a bf16 is negative exactly when its
 // bit pattern is negative as an int16, so a packed signed max with 0 zeroes the

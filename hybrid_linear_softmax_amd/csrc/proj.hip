@@ -36,8 +36,6 @@ constexpr int kTK = 64;    // K per step
 constexpr int kGroupM = 4; // token tiles per ordering group
 constexpr int kLP = kTK + 8;  // LDS pitch (elements) of a 64-wide row
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 struct ProjShape {
   int64_t M;      // tokens B * N
   int64_t Nf;     // output features (4C or C)
