@@ -282,13 +282,15 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     constexpr int NQK = 2 * KS;          // logit MFMAs per block
     constexpr int PER = 16 / NQK;        // probability pairs per logit MFMA
     static_assert(PER * NQK == 16, "16 probability pairs per lane and block");
-    bf16x8 kf[2] = {kfrag(0), kfrag(1)};
+    bf16x8 kf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) kf[i] = kfrag(i);
     uint32_t pk[16];
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int t = i & 1, st = i >> 1;
-      const bf16x8 a = kf[i & 1];
-      if (i + 2 < NQK) kf[i & 1] = kfrag(i + 2);
+      const bf16x8 a = kf[i % 2];
+      if (i + 2 < NQK) kf[i % 2] = kfrag(i + 2);
       snext[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], snext[t], 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
@@ -319,13 +321,15 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     constexpr int NPV = 4 * RB;          // PV MFMAs per block
     constexpr int PERM = 32 / NPV;       // logits of the row max per PV MFMA
     static_assert(PERM * NPV == 32 && PERM % 2 == 0, "32 logits per lane and block");
-    bf16x8 vf[2] = {vfrag(0), vfrag(1)};
+    bf16x8 vf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vf[i] = vfrag(i);
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int rb = i % RB, q = i / RB, t = q >> 1, tt = q & 1;
-      const bf16x8 a = vf[i & 1];
-      if (i + 2 < NPV) vf[i & 1] = vfrag(i + 2);
+      const bf16x8 a = vf[i % 2];
+      if (i + 2 < NPV) vf[i % 2] = vfrag(i + 2);
       o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t][tt], o[rb], 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < PERM; u += 2) {
