@@ -55,6 +55,17 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 
+// Block order of the sparse anchor: the blocks in flight all belong to one
+// (b, h), spread over the 8 XCDs (blocks are dispatched round-robin), and each
+// XCD walks a contiguous run of that head's query blocks.  Neighbouring query
+// blocks share their local key windows in the XCD's L2, and every XCD reads the
+// head's global frames, which then stay in the shared last-level cache.  (The
+// dense anchor keeps xcd_remap: every query block reads every key there.)
+__device__ __forceinline__ int64_t head_runs_remap(int64_t i, int64_t qblocks) {
+  const int64_t hh = i / qblocks, j = i % qblocks, per = qblocks / 8;
+  return hh * qblocks + (j < per * 8 ? (j % 8) * per + j / 8 : j);
+}
+
 // SPARSE: the query block walks the key blocks listed for it in a CSR pattern
 // (blk_off / blk_idx) instead of all key blocks.  Listed indices outside
 // [0, ceil(N/64)) are read as empty blocks (buffer loads past the head read
@@ -85,7 +96,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const int64_t id = xcd_remap(blockIdx.x, total);
+  const int64_t id = SPARSE ? head_runs_remap(blockIdx.x, qblocks) : xcd_remap(blockIdx.x, total);
   const int64_t bh = id / qblocks;
   const int64_t q0 = (id % qblocks) * kBr + 32 * wave;
   const int64_t base = bh * N * D;
