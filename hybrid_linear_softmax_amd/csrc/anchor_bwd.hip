@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
                                                       const bf16_t* __restrict__ V, const bf16_t* __restrict__ da,
                                                       const float* __restrict__ lse, const float* __restrict__ Dv,
                                                       bf16_t* __restrict__ dQ, int64_t N, int64_t qblocks,
-                                                      int64_t total, float c) {
+                                                      float c) {
   constexpr int NT = 256, BK = 64;
   constexpr int KP = D + 8, TP = BK + 8, FG = D / 8;
   constexpr int KCH = BK * FG / NT;     // 16-byte chunks per thread per tile
@@ -113,7 +113,9 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int64_t id = xcd_remap(blockIdx.x, total);
+  // plain dispatch order: the blocks in flight cover one (b, h) across all
+  // XCDs, which measured faster here than one head per XCD (xcd_remap)
+  const int64_t id = blockIdx.x;
   const int64_t bh = id / qblocks;
   const int64_t qrow = (id % qblocks) * 128 + 32 * wave + l32;
   const int64_t base = bh * N * D;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
                                                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ da,
                                                           const float* __restrict__ lse, const float* __restrict__ Dv,
                                                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int64_t N,
-                                                          int64_t kblocks, int64_t total, float c) {
+                                                          int64_t kblocks, float c) {
   constexpr int NT = 512, BQ = 64, BKW = 128;
   constexpr int KP = D + 8, TP = BQ + 8, FG = D / 8;
   constexpr int KCHW = BKW * FG / NT;
@@ -260,7 +262,9 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
   const int l32 = lane & 31, h = lane >> 5;
   const int kw = wave & 3;   // 32-key group
   const int th = wave >> 2;  // 32-query half of each step
-  const int64_t id = xcd_remap(blockIdx.x, total);
+  // plain dispatch order: the blocks in flight cover one (b, h) across all
+  // XCDs, which measured faster here than one head per XCD (xcd_remap)
+  const int64_t id = blockIdx.x;
   const int64_t bh = id / kblocks;
   const int64_t kbase = (id % kblocks) * BKW;
   const int64_t krow = kbase + 32 * kw + l32;
@@ -565,14 +569,14 @@ hipError_t launch_softmax_backward(bool bf16, int d, const void* Q, const void* 
     const int64_t kb = (N + 127) / 128, tk = BH * kb;
     if (d == 128) {
       sm_bwd_dq_bf16<128><<<dim3(static_cast<unsigned>(tq)), dim3(256), 0, s>>>(q, k, v, a, lse, Dv,
-                                                                                 static_cast<bf16_t*>(dQ), N, qb, tq, c);
+                                                                                 static_cast<bf16_t*>(dQ), N, qb, c);
       sm_bwd_dkv_bf16<128><<<dim3(static_cast<unsigned>(tk)), dim3(512), 0, s>>>(
-          q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, tk, c);
+          q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, c);
     } else {
       sm_bwd_dq_bf16<64><<<dim3(static_cast<unsigned>(tq)), dim3(256), 0, s>>>(q, k, v, a, lse, Dv,
-                                                                                static_cast<bf16_t*>(dQ), N, qb, tq, c);
+                                                                                static_cast<bf16_t*>(dQ), N, qb, c);
       sm_bwd_dkv_bf16<64><<<dim3(static_cast<unsigned>(tk)), dim3(512), 0, s>>>(
-          q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, tk, c);
+          q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, c);
     }
   } else {
     const float* q = static_cast<const float*>(Q);
