@@ -55,10 +55,15 @@ int check_buffers(const void* const* in, int n_in, size_t in_bytes, const void* 
   return HA_OK;
 }
 
-int check_workspace(const Problem& p, const void* ws, size_t ws_bytes) {
+// The linear layer's workspace: present, large enough, aligned, and disjoint
+// from the n tensors of the call (t[i] spanning t_bytes[i] bytes).
+int check_workspace(const Problem& p, const void* ws, size_t ws_bytes, const void* const* t,
+                    const size_t* t_bytes, int n) {
   const size_t need = ha::linear_ws(p.BH, p.N, static_cast<int>(p.d), p.bf16).total;
   if (ws == nullptr || ws_bytes < need) return HA_EWORKSPACE;
   if (misaligned(ws)) return HA_EALIGN;
+  for (int i = 0; i < n; ++i)
+    if (overlaps(ws, need, t[i], t_bytes[i])) return HA_EINVAL;
   return HA_OK;
 }
 
@@ -168,7 +173,7 @@ extern "C" {
 HA_API const char* hybrid_attn_strerror(int status) {
   switch (status) {
     case HA_OK: return "success";
-    case HA_EINVAL: return "invalid argument (size, null pointer or output overlapping an input)";
+    case HA_EINVAL: return "invalid argument (size, null pointer, or an output or workspace overlapping another buffer)";
     case HA_EUNSUPPORTED: return "unsupported head dimension or dtype (d must be 64 or 128; dtype bf16 or f32)";
     case HA_EALIGN: return "pointer not 16-byte aligned";
     case HA_EWORKSPACE: return "workspace missing or smaller than hybrid_attn_workspace_bytes()";
@@ -203,8 +208,12 @@ HA_API int hybrid_attn_kv_state(const void* K, const void* V, float* S, float* z
     return HA_EALIGN;
   }
   if (overlaps(S, s_bytes, z, z_bytes)) return HA_EINVAL;
-  st = check_workspace(p, workspace, workspace_bytes);
-  if (st != HA_OK) return st;
+  {
+    const void* t[4] = {K, V, S, z};
+    const size_t tb[4] = {p.tensor_bytes, p.tensor_bytes, s_bytes, z_bytes};
+    st = check_workspace(p, workspace, workspace_bytes, t, tb, 4);
+    if (st != HA_OK) return st;
+  }
 
   const ha::LinearWs L = ha::linear_ws(p.BH, p.N, d, p.bf16);
   char* w = static_cast<char*>(workspace);
@@ -227,7 +236,9 @@ HA_API int hybrid_attn_linear(const void* Q, const void* K, const void* V, const
   const void* in[4] = {Q, K, V, G};
   st = check_buffers(in, 4, p.tensor_bytes, O, p.tensor_bytes);
   if (st != HA_OK) return st;
-  st = check_workspace(p, workspace, workspace_bytes);
+  const void* t[5] = {Q, K, V, G, O};
+  const size_t tb[5] = {p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes};
+  st = check_workspace(p, workspace, workspace_bytes, t, tb, 5);
   if (st != HA_OK) return st;
   return run_linear(p, Q, K, V, G, O, workspace, stream);
 }
@@ -285,7 +296,9 @@ HA_API int hybrid_attn_group_timed(const void* Q4, const void* K4, const void* V
   const void* in[4] = {Q4, K4, V4, G4};
   st = check_buffers(in, 4, group_bytes, O4, group_bytes);
   if (st != HA_OK) return st;
-  st = check_workspace(p, workspace, workspace_bytes);
+  const void* t[5] = {Q4, K4, V4, G4, O4};
+  const size_t tb[5] = {group_bytes, group_bytes, group_bytes, group_bytes, group_bytes};
+  st = check_workspace(p, workspace, workspace_bytes, t, tb, 5);
   if (st != HA_OK) return st;
 
   int kinds[4];

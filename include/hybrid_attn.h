@@ -61,7 +61,8 @@ typedef enum ha_status {
   HA_OK = 0,
   HA_EUNSUPPORTED = -2, /* d not 64 or 128, or unknown dtype                      */
   HA_EINVAL = -1,       /* negative or too large B/H/N, null pointer, output that
-                           overlaps an input, null kinds array                   */
+                           overlaps an input, workspace that overlaps a tensor of
+                           the call, null kinds array                            */
   HA_EALIGN = -3,       /* a tensor or workspace pointer not 16-byte aligned      */
   HA_EWORKSPACE = -4,   /* workspace null or smaller than hybrid_attn_workspace_bytes */
   HA_EHIP = -5          /* a kernel launch or event record failed                 */

@@ -98,6 +98,17 @@ def test_workspace_errors(lib):
     assert lib.hybrid_attn_kv_state(K, V, None, Z, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
     assert lib.hybrid_attn_kv_state(K, V, S, S + 64, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
     assert lib.hybrid_attn_kv_state(K, V, K, Z, 1, 2, 100, 64, HA_BF16, WS, need, None) == EINVAL
+    # a workspace overlapping any tensor of the call is rejected (only rejected
+    # calls here: a valid one would launch on the fake addresses)
+    tensor = 1 * 2 * 100 * 64 * 2
+    for t in (Q, K, V, G, O):
+        assert _linear(lib, ws=t + 256) == EINVAL, t
+        assert _linear(lib, ws=t - need + 256 if t - need + 256 > 0 else t) == EINVAL, t
+    for t in (K, V, S, Z):
+        assert lib.hybrid_attn_kv_state(K, V, S, Z, 1, 2, 100, 64, HA_BF16, t + 256, need, None) == EINVAL, t
+    # the size check runs before the overlap check
+    assert _linear(lib, ws=Q + 256, nb=need - 1) == EWS
+    assert tensor < GB
 
 
 def test_blocksparse_pattern_errors(lib):
@@ -127,6 +138,9 @@ def test_group_errors(lib):
     evs = (ctypes.c_void_p * 5)(1, 2, None, 4, 5)
     assert lib.hybrid_attn_group_timed(*args, WS, need, None, evs) == EINVAL
     assert lib.hybrid_attn_group(Q, K, V, G, O, 1, 2, 100, 80, HA_BF16, WS, need, None) == EUNSUP
+    # the workspace may not overlap any of the stacked tensors, layer 3 included
+    assert lib.hybrid_attn_group(*args, O + 3 * layer_bytes, need, None) == EINVAL
+    assert lib.hybrid_attn_group(*args, Q + 256, need, None) == EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
