@@ -63,19 +63,54 @@ def _dtype_code(t: torch.Tensor) -> int:
         raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32") from None
 
 
+def _on_current_device(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the library launches on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
 def _tensors(names, tensors, ndim):
     ref = tensors[0]
     for n, t in zip(names, tensors):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{n} must be a torch.Tensor")
-        if not t.is_cuda:
-            raise ValueError(f"{n} must be a device tensor")
+        _on_current_device(n, t)
         if t.dim() != ndim or t.shape != ref.shape or t.dtype != ref.dtype:
             raise ValueError(f"{n}: expected shape {tuple(ref.shape)} / dtype {ref.dtype}, "
                              f"got {tuple(t.shape)} / {t.dtype}")
         if not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous")
     return ref
+
+
+def _like(name, t, shape, dtype, device):
+    """A caller-supplied tensor: a contiguous `shape` / `dtype` tensor on `device`
+    (the kernels write or read exactly that many elements)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device or tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {tuple(shape)} {dtype} tensor on {device}, got "
+                         f"{tuple(t.shape)} {t.dtype} on {t.device}{'' if t.is_contiguous() else ', not contiguous'}")
+    return t
+
+
+def _out(name, t, shape, dtype, device):
+    """An output: allocated when the caller passes None, else checked by _like."""
+    if t is None:
+        return torch.empty(tuple(shape), dtype=dtype, device=device)
+    return _like(name, t, shape, dtype, device)
+
+
+def _ws_tensor(workspace, need, device):
+    """The workspace: allocated when the caller passes None, else a contiguous
+    tensor on `device` (its byte size is checked by the library)."""
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return workspace
 
 
 def _stream(stream):
@@ -93,9 +128,7 @@ def workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) -> int
 
 
 def _workspace(B, H, N, d, dtype, device, workspace):
-    need = workspace_bytes(B, H, N, d, dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    workspace = _ws_tensor(workspace, workspace_bytes(B, H, N, d, dtype), device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -103,10 +136,8 @@ def hybrid_attn_kv_state(K, V, S=None, z=None, workspace=None, stream=None):
     """Float32 state S [B, H, d, d] and normaliser z [B, H, d] of K, V [B, H, N, d]."""
     ref = _tensors(("K", "V"), (K, V), 4)
     B, H, N, d = ref.shape
-    if S is None:
-        S = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
-    if z is None:
-        z = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    S = _out("S", S, (B, H, d, d), torch.float32, ref.device)
+    z = _out("z", z, (B, H, d), torch.float32, ref.device)
     ws, nbytes = _workspace(B, H, N, d, ref.dtype, ref.device, workspace)
     _check(_lib.load().hybrid_attn_kv_state(_ptr(K), _ptr(V), _ptr(S), _ptr(z), B, H, N, d,
                                             _dtype_code(ref), _ptr(ws), nbytes, _stream(stream)),
@@ -118,7 +149,7 @@ def hybrid_attn_linear(Q, K, V, G, O=None, workspace=None, stream=None):
     """One gated linear-attention layer; Q, K, V, G, O: [B, H, N, d]."""
     ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
     B, H, N, d = ref.shape
-    O = torch.empty_like(ref) if O is None else O
+    O = _out("O", O, ref.shape, ref.dtype, ref.device)
     ws, nbytes = _workspace(B, H, N, d, ref.dtype, ref.device, workspace)
     _check(_lib.load().hybrid_attn_linear(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), B, H, N, d,
                                           _dtype_code(ref), _ptr(ws), nbytes, _stream(stream)),
@@ -130,7 +161,7 @@ def hybrid_attn_softmax(Q, K, V, G, O=None, stream=None):
     """One gated softmax anchor layer; Q, K, V, G, O: [B, H, N, d]."""
     ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
     B, H, N, d = ref.shape
-    O = torch.empty_like(ref) if O is None else O
+    O = _out("O", O, ref.shape, ref.dtype, ref.device)
     _check(_lib.load().hybrid_attn_softmax(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), B, H, N, d,
                                            _dtype_code(ref), _stream(stream)),
            "hybrid_attn_softmax")
@@ -152,7 +183,7 @@ def hybrid_attn_softmax_blocksparse(Q, K, V, G, block_offsets, block_indices, O=
             raise ValueError(f"{n} must be contiguous on {ref.device}")
     if block_offsets.numel() != nqb + 1:
         raise ValueError(f"block_offsets: {nqb + 1} entries expected for N={N}, got {block_offsets.numel()}")
-    O = torch.empty_like(ref) if O is None else O
+    O = _out("O", O, ref.shape, ref.dtype, ref.device)
     n_idx = block_indices.numel()
     idx_ptr = _ptr(block_indices) if n_idx > 0 else ctypes.c_void_p(None)
     _check(_lib.load().hybrid_attn_softmax_blocksparse(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), B, H, N,
@@ -170,7 +201,7 @@ def hybrid_attn_group(Q4, K4, V4, G4, O4=None, workspace=None, stream=None, even
     L, B, H, N, d = ref.shape
     if L != 4:
         raise ValueError(f"a group has 4 layers, got {L}")
-    O4 = torch.empty_like(ref) if O4 is None else O4
+    O4 = _out("O4", O4, ref.shape, ref.dtype, ref.device)
     ws, nbytes = _workspace(B, H, N, d, ref.dtype, ref.device, workspace)
     lib = _lib.load()
     args = (_ptr(Q4), _ptr(K4), _ptr(V4), _ptr(G4), _ptr(O4), B, H, N, d, _dtype_code(ref),
@@ -197,15 +228,14 @@ def hybrid_attn_group_schedule():
 
 
 def _check_weight(name, t, shape, ref):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if tuple(t.shape) != tuple(shape) or t.dtype != ref.dtype or not t.is_contiguous():
-        raise ValueError(f"{name}: expected contiguous {tuple(shape)} / {ref.dtype}, got {tuple(t.shape)} / {t.dtype}")
+    _like(name, t, shape, ref.dtype, ref.device)
 
 
 def _block_dims(x, heads):
     if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 3 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [B, N, C] device tensor")
+    _on_current_device("x", x)
+    _dtype_code(x)
     B, N, C = x.shape
     if heads <= 0 or C % heads:
         raise ValueError(f"heads={heads} must divide C={C}")
@@ -222,9 +252,7 @@ def hybrid_attn_proj_in(x, W_in, heads, Q=None, K=None, V=None, G=None, stream=N
     `heads` heads; x: [B, N, C], W_in: [4C, C]."""
     B, N, C, d = _block_dims(x, heads)
     _check_weight("W_in", W_in, (4 * C, C), x)
-    outs = [torch.empty((B, heads, N, d), dtype=x.dtype, device=x.device) if t is None else t
-            for t in (Q, K, V, G)]
-    _tensors(("Q", "K", "V", "G"), outs, 4)
+    outs = [_out(n, t, (B, heads, N, d), x.dtype, x.device) for n, t in zip("QKVG", (Q, K, V, G))]
     _check(_lib.load().hybrid_attn_proj_in(_ptr(x), _ptr(W_in), *(_ptr(t) for t in outs), B, heads, N, d,
                                            _dtype_code(x), _stream(stream)),
            "hybrid_attn_proj_in")
@@ -240,7 +268,7 @@ def hybrid_attn_proj_out(O, W_out, x, x_out=None, stream=None):
     if tuple(x.shape) != (B, N, H * d) or x.dtype != O.dtype:
         raise ValueError(f"x: expected {(B, N, H * d)} / {O.dtype}, got {tuple(x.shape)} / {x.dtype}")
     _check_weight("W_out", W_out, (H * d, H * d), x)
-    x_out = torch.empty_like(x) if x_out is None else x_out
+    x_out = _out("x_out", x_out, x.shape, x.dtype, x.device)
     _check(_lib.load().hybrid_attn_proj_out(_ptr(O), _ptr(W_out), _ptr(x), _ptr(x_out), B, H, N, d,
                                             _dtype_code(x), _stream(stream)),
            "hybrid_attn_proj_out")
@@ -254,15 +282,23 @@ def hybrid_attn_block(x, W_in4, W_out4, heads, x_out=None, workspace=None, strea
     B, N, C, d = _block_dims(x, heads)
     _check_weight("W_in4", W_in4, (4, 4 * C, C), x)
     _check_weight("W_out4", W_out4, (4, C, C), x)
-    x_out = torch.empty_like(x) if x_out is None else x_out
-    need = block_workspace_bytes(B, heads, N, d, x.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    x_out = _out("x_out", x_out, x.shape, x.dtype, x.device)
+    workspace = _ws_tensor(workspace, block_workspace_bytes(B, heads, N, d, x.dtype), x.device)
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib.load().hybrid_attn_block(_ptr(x), _ptr(W_in4), _ptr(W_out4), _ptr(x_out), B, heads, N, d,
                                          _dtype_code(x), _ptr(workspace), nbytes, _stream(stream)),
            "hybrid_attn_block")
     return x_out
+
+
+def _grads(grads, ref):
+    """The four gradient outputs dQ, dK, dV, dG, each shaped like `ref`."""
+    if grads is None:
+        return [torch.empty_like(ref) for _ in range(4)]
+    grads = list(grads)
+    if len(grads) != 4:
+        raise ValueError("grads: four tensors (dQ, dK, dV, dG) expected")
+    return [_like(n, t, ref.shape, ref.dtype, ref.device) for n, t in zip(("dQ", "dK", "dV", "dG"), grads)]
 
 
 def linear_backward_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) -> int:
@@ -275,11 +311,8 @@ def hybrid_attn_linear_backward(Q, K, V, G, dO, grads=None, workspace=None, stre
     (all [B, H, N, d]).  `grads` may hold four preallocated output tensors."""
     ref = _tensors(("Q", "K", "V", "G", "dO"), (Q, K, V, G, dO), 4)
     B, H, N, d = ref.shape
-    grads = [torch.empty_like(ref) for _ in range(4)] if grads is None else list(grads)
-    _tensors(("dQ", "dK", "dV", "dG"), grads, 4)
-    need = linear_backward_workspace_bytes(B, H, N, d, ref.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ref.device)
+    grads = _grads(grads, ref)
+    workspace = _ws_tensor(workspace, linear_backward_workspace_bytes(B, H, N, d, ref.dtype), ref.device)
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib.load().hybrid_attn_linear_backward(*(_ptr(t) for t in (Q, K, V, G, dO)), *(_ptr(t) for t in grads),
                                                    B, H, N, d, _dtype_code(ref), _ptr(workspace), nbytes,
@@ -293,10 +326,8 @@ def hybrid_attn_softmax_lse(Q, K, V, G, O=None, lse=None, stream=None):
     the forward pass whose outputs hybrid_attn_softmax_backward consumes."""
     ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
     B, H, N, d = ref.shape
-    O = torch.empty_like(ref) if O is None else O
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=ref.device) if lse is None else lse
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    O = _out("O", O, ref.shape, ref.dtype, ref.device)
+    lse = _out("lse", lse, (B, H, N), torch.float32, ref.device)
     _check(_lib.load().hybrid_attn_softmax_lse(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), _ptr(lse), B, H, N, d,
                                                _dtype_code(ref), _stream(stream)),
            "hybrid_attn_softmax_lse")
@@ -313,13 +344,9 @@ def hybrid_attn_softmax_backward(Q, K, V, G, O, dO, lse, grads=None, workspace=N
     hybrid_attn_softmax_lse."""
     ref = _tensors(("Q", "K", "V", "G", "O", "dO"), (Q, K, V, G, O, dO), 4)
     B, H, N, d = ref.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    grads = [torch.empty_like(ref) for _ in range(4)] if grads is None else list(grads)
-    _tensors(("dQ", "dK", "dV", "dG"), grads, 4)
-    need = softmax_backward_workspace_bytes(B, H, N, d, ref.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ref.device)
+    _like("lse", lse, (B, H, N), torch.float32, ref.device)
+    grads = _grads(grads, ref)
+    workspace = _ws_tensor(workspace, softmax_backward_workspace_bytes(B, H, N, d, ref.dtype), ref.device)
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib.load().hybrid_attn_softmax_backward(*(_ptr(t) for t in (Q, K, V, G, O, dO, lse)),
                                                     *(_ptr(t) for t in grads), B, H, N, d, _dtype_code(ref),
@@ -332,17 +359,25 @@ def hybrid_attn_attnres_mix(summaries, x, w, h=None, stream=None):
     """AttnRes mixture h [B, N, C] over the candidates summaries [M, B, N, C]
     (M may be 0; pass None) and x, with routing vector w (float32 [C])."""
     B, N, C = _block_dims(x, 1)[:3]
-    M = 0 if summaries is None else summaries.shape[0]
-    if M:
-        if tuple(summaries.shape[1:]) != (B, N, C) or summaries.dtype != x.dtype or not summaries.is_contiguous():
-            raise ValueError("summaries must be a contiguous [M, B, N, C] tensor of x's dtype")
-    if w.dtype != torch.float32 or tuple(w.shape) != (C,) or not w.is_contiguous():
-        raise ValueError("w must be a contiguous float32 [C] tensor")
-    h = torch.empty_like(x) if h is None else h
+    M = _summaries(summaries, x)
+    _like("w", w, (C,), torch.float32, x.device)
+    h = _out("h", h, x.shape, x.dtype, x.device)
     _check(_lib.load().hybrid_attn_attnres_mix(_ptr(summaries) if M else ctypes.c_void_p(None), M, _ptr(x), _ptr(w),
                                                _ptr(h), B, N, C, _dtype_code(x), _stream(stream)),
            "hybrid_attn_attnres_mix")
     return h
+
+
+def _summaries(summaries, x):
+    """Number of completed-block summaries: 0 for None, else M of a contiguous
+    [M, B, N, C] tensor shaped and typed like x."""
+    if summaries is None:
+        return 0
+    if not isinstance(summaries, torch.Tensor) or summaries.dim() != 4:
+        raise ValueError("summaries must be an [M, B, N, C] tensor or None")
+    M = summaries.shape[0]
+    _like("summaries", summaries, (M, *x.shape), x.dtype, x.device)
+    return M
 
 
 def block_routed_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) -> int:
@@ -356,13 +391,10 @@ def hybrid_attn_block_routed(x, summaries, w_route, W_in4, W_out4, heads, x_out=
     B, N, C, d = _block_dims(x, heads)
     _check_weight("W_in4", W_in4, (4, 4 * C, C), x)
     _check_weight("W_out4", W_out4, (4, C, C), x)
-    if w_route.dtype != torch.float32 or tuple(w_route.shape) != (4, C) or not w_route.is_contiguous():
-        raise ValueError("w_route must be a contiguous float32 [4, C] tensor")
-    M = 0 if summaries is None else summaries.shape[0]
-    x_out = torch.empty_like(x) if x_out is None else x_out
-    need = block_routed_workspace_bytes(B, heads, N, d, x.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _like("w_route", w_route, (4, C), torch.float32, x.device)
+    M = _summaries(summaries, x)
+    x_out = _out("x_out", x_out, x.shape, x.dtype, x.device)
+    workspace = _ws_tensor(workspace, block_routed_workspace_bytes(B, heads, N, d, x.dtype), x.device)
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib.load().hybrid_attn_block_routed(_ptr(x), _ptr(summaries) if M else ctypes.c_void_p(None), M,
                                                 _ptr(w_route), _ptr(W_in4), _ptr(W_out4), _ptr(x_out), B, heads, N, d,

@@ -253,3 +253,15 @@ def test_attnres_errors(lib):
     assert blk(xo=SUM + tb) == EINVAL               # output inside the summaries
     assert blk(ws=None) == EWS and blk(nb=need - 1) == EWS
     assert blk(ws=SUM - 512) == EINVAL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    import hybrid_linear_softmax_amd as ha
+    t = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        ha.hybrid_attn_softmax(t, t, t, t)
+    with pytest.raises(ValueError, match="device tensor"):
+        ha.hybrid_attn_linear(t, t, t, t)
+    with pytest.raises(ValueError, match="device tensor"):
+        ha.hybrid_attn_proj_in(torch.zeros((1, 8, 128), dtype=torch.bfloat16), torch.zeros((512, 128)), 2)
