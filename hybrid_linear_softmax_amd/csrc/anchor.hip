@@ -29,7 +29,11 @@
 //    below 256, exact enough in fp32 and bf16), which after the first blocks is
 //    almost never;
 //  * row sums are taken over the bf16-rounded probabilities with v_dot2 (two per
-//    instruction), i.e. over exactly the weights the PV product uses.
+//    instruction), i.e. over exactly the weights the PV product uses.  Each key
+//    block is summed on its own and joins the running sum through compensated
+//    (Kahan) addition: a lane's sum covers N/2 keys, and at millions of keys a
+//    plain fp32 sum rounds every near-one pair the same way (its ulp reaches
+//    0.5 past 2^22), which biases the denominator by about one percent.
 #include <type_traits>
 
 #include "ha_device.h"
@@ -153,6 +157,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     for (int r = 0; r < 16; ++r) o[rb][r] = 0.f;
   float m = -INFINITY;  // running max of the raw logits of this lane's query
   float lsum = 0.f;     // running sum of this lane's probabilities (half the keys)
+  float lcomp = 0.f;    // its Kahan compensation: the low-order part lost so far
 
   // Software pipeline over 64-key blocks j: each step issues the logit MFMAs of
   // block j+1 (independent work) while the softmax of block j runs on the VALU,
@@ -192,6 +197,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
       m = m_new;
       lsum *= alpha;
+      lcomp *= alpha;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -271,9 +277,11 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   // below 64).  The step is written in the order it should issue: each logit
   // MFMA of block j+1 is followed by two probabilities of block j (exp2, bf16
   // pack, row-sum dot), each PV MFMA of block j by a slice of block j+1's row
-  // max, K/V fragments read two MFMAs ahead.  Empty asm statements that consume
-  // each slice's result pin it between its MFMAs: left alone, the compiler
-  // sinks the VALU work to its first use and clusters the MFMAs.
+  // max (the first three also carry the compensated addition of block j's
+  // probability sum), K/V fragments read two MFMAs ahead.  Empty asm
+  // statements that consume each slice's result pin it between its MFMAs: left
+  // alone, the compiler sinks the VALU work to its first use and clusters the
+  // MFMAs.
   auto step = [&](int64_t j, int64_t k1, int64_t k2, int lim1, f32x16 (&scur)[2], f32x16 (&snext)[2],
                   auto masked) {
     const int kb = static_cast<int>((j + 1) & 1);
@@ -297,6 +305,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 2; ++i) kf[i] = kfrag(i);
     uint32_t pk[16];
+    float lblk = 0.f;  // this block's probabilities, before they join lsum
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int t = i & 1, st = i >> 1;
@@ -309,8 +318,8 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
         const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[e0 >> 4][e0 & 15], c, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[e1 >> 4][e1 & 15], c, -mc));
         pk[pi] = pack_bf16(p0, p1);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[pi]), one, lsum, false);
-        asm volatile("" : "+v"(pk[pi]), "+v"(lsum));
+        lblk = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[pi]), one, lblk, false);
+        asm volatile("" : "+v"(pk[pi]), "+v"(lblk));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -335,6 +344,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     bf16x8 vf[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) vf[i] = vfrag(i);
+    float ky, kt;  // Kahan terms of the block sum, spread over the first PV MFMAs
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
@@ -347,6 +357,9 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
         const int e0 = i * PERM + u, e1 = e0 + 1;
         mx = fmaxf(mx, fmaxf(snext[e0 >> 4][e0 & 15], snext[e1 >> 4][e1 & 15]));
       }
+      if (i == 0) { ky = lblk - lcomp; asm volatile("" : "+v"(ky)); }
+      if (i == 1) { kt = lsum + ky; asm volatile("" : "+v"(kt)); }
+      if (i == 2) { lcomp = (kt - lsum) - ky; lsum = kt; asm volatile("" : "+v"(lcomp), "+v"(lsum)); }
       asm volatile("" : "+v"(mx));
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -383,7 +396,8 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     }
   }
 
-  const float l = lsum + __shfl_xor(lsum, 32);
+  const float lrow = lsum - lcomp;
+  const float l = lrow + __shfl_xor(lrow, 32);
   // (sparse) a query block with no valid key has l = 0 and gets O = 0
   const float inv = (SPARSE && !(l > 0.f)) ? 0.f : __builtin_amdgcn_rcpf(l);
   // natural log of sum_j exp(q . k_j / sqrt(d)) for the backward pass:
@@ -435,6 +449,7 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  float lc = 0.f;  // Kahan compensation of l (the sum runs over up to N keys)
   const int64_t nkb = (N + kBc - 1) / kBc;
   int64_t list_beg = 0, nsteps = (N + BK - 1) / BK;
   if (SPARSE) {
@@ -472,17 +487,23 @@ __global__ __launch_bounds__(128) void anchor_f32(const float* __restrict__ Q,
     if (m_new == -INFINITY) continue;  // no valid key yet (sparse tail halves)
     const float alpha = expf(m - m_new);
     l *= alpha;
+    lc *= alpha;
 #pragma unroll
     for (int e = 0; e < HD; ++e) acc[e] *= alpha;
+    float lb = 0.f;
 #pragma unroll
     for (int j = 0; j < BK; ++j) {
       const float p = expf(sc[j] - m_new);
-      l += p;
+      lb += p;
 #pragma unroll
       for (int e = 0; e < HD; ++e) acc[e] = fmaf(p, sV[j][half * HD + e], acc[e]);
     }
+    const float y = lb - lc, t = l + y;
+    lc = (t - l) - y;
+    l = t;
     m = m_new;
   }
+  l -= lc;
   if (lse != nullptr && qrow < N && half == 0) lse[bh * N + qrow] = m + logf(l);
   if (qrow < N) {
 #pragma unroll
