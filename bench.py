@@ -29,12 +29,22 @@ of the outputs of blocks 0 .. k-1 and the current stream.
 hybrid_attn_block on a residual stream x [B, N, H*d] with synthetic weights
 (four sub-layers, each Q/K/V/G projection, the layer, output projection and
 residual); one extra untimed-for-value pass times each stage on its own.
+
+Every line also carries `achievable` -- what this part sustains, measured after
+the timed steps with the library's probe kernels (an MFMA loop and HBM read and
+copy streams, include/ha_probe.h) -- with the roofline's rate against it as
+`roofline.frac_of_achievable`, and `telemetry`: the GPU clock and socket power
+sampled through amdsmi while the step repeats, untimed, for about 2.5 s after
+the timed steps (the device refreshes those metrics about once a second; null
+where that interface is unavailable).
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +65,187 @@ def anchor_source_hash() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+class Telemetry:
+    """GPU clock (MHz) and socket power (W) sampled through amdsmi on a host
+    thread.  The device refreshes these metrics about once a second, so samples
+    are told apart by the metrics' own timestamp and only fresh ones count.
+    summary() is None when amdsmi cannot be used (no driver, no permission, or
+    the device is not found)."""
+
+    def __init__(self, device=0, period_s=0.1):
+        self.period_s = period_s
+        self.samples = []          # (metrics timestamp or None, clock MHz, power W)
+        self.power_limit_w = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._smi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._handle = self._find_handle(amdsmi, device)
+            limit = amdsmi.amdsmi_get_power_info(self._handle).get("power_limit")
+            if isinstance(limit, (int, float)) and limit > 0:
+                self.power_limit_w = round(limit / 1e6, 1) if limit > 1e5 else float(limit)   # reported in uW
+        except Exception:
+            self._handle = None
+
+    @property
+    def available(self):
+        return self._handle is not None
+
+    @staticmethod
+    def _find_handle(amdsmi, device):
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) == 1:
+            return handles[0]
+        import torch
+        bus = getattr(torch.cuda.get_device_properties(device), "pci_bus_id", None)
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)      # "dddd:bb:dd.f"
+            if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                return h
+        return None
+
+    def _sample(self):
+        smi, h = self._smi, self._handle
+        num = lambda v: v if isinstance(v, (int, float)) else None   # noqa: E731
+        try:
+            m = smi.amdsmi_get_gpu_metrics_info(h)
+            return (num(m.get("system_clock_counter")), num(m.get("current_gfxclk")),
+                    num(m.get("current_socket_power")))
+        except Exception:
+            clk = smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX).get("clk")
+            return (None, num(clk), num(smi.amdsmi_get_power_info(h).get("current_socket_power")))
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._sample())
+            except Exception:
+                pass
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def summary(self):
+        s = summarize_telemetry(self.samples)
+        if s is not None and self.power_limit_w is not None:
+            s["power_limit_w"] = self.power_limit_w
+        return s
+
+
+def summarize_telemetry(samples):
+    """Median / min / max over the fresh (timestamp, clock MHz, power W) samples:
+    the first one (it may predate the window) and repeats of a timestamp are
+    dropped.  None when nothing fresh was seen."""
+    fresh, last = [], object()
+    for i, (ts, clk, pw) in enumerate(samples):
+        if i == 0 or (ts is not None and ts == last):
+            last = ts
+            continue
+        last = ts
+        fresh.append((clk, pw))
+    out = {}
+    for i, key in ((0, "gfx_clock_mhz"), (1, "socket_power_w")):
+        vals = [f[i] for f in fresh if f[i] is not None]
+        if vals:
+            out[key] = {"median": round(statistics.median(vals), 1), "min": round(min(vals), 1),
+                        "max": round(max(vals), 1)}
+    if not out:
+        return None
+    out["fresh_samples"] = len(fresh)
+    return out
+
+
+def sample_telemetry(step, dev, seconds=2.5):
+    """Clock and power while `step` repeats (untimed) for at least `seconds`
+    and at least once, after the timed steps; None without amdsmi."""
+    import torch
+
+    tele = Telemetry(dev.index)
+    if not tele.available:
+        return None
+    n = 0
+    with tele:
+        t_end = time.time() + seconds
+        while n == 0 or time.time() < t_end:
+            step()
+            torch.cuda.synchronize()
+            n += 1
+    s = tele.summary()
+    if s is not None:
+        s["window"] = f"{n} untimed steps over >= {seconds} s after the timed steps"
+    return s
+
+
+def achievable_peaks(dev, reps=3):
+    """What this part sustains, from the library's probe kernels: the bf16 MFMA
+    loop (TFLOP/s) and HBM streams over 1 GiB buffers (GB/s, read + written);
+    the best of `reps` event-timed runs (each of `launches` back-to-back calls,
+    so that launch gaps do not count) after one warm-up each."""
+    import torch
+
+    import hybrid_linear_softmax_amd as ha
+
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def best(fn, launches=1):
+        fn()
+        torch.cuda.synchronize()
+        rates = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            work = sum(fn() for _ in range(launches))
+            e1.record()
+            torch.cuda.synchronize()
+            rates.append(work / (e0.elapsed_time(e1) / 1e3))
+        return max(rates)
+
+    blocks, iters = 1024, 131072
+    out = {"mfma_bf16_tflops": round(best(lambda: ha.probe_mfma(blocks, iters, sink)) / 1e12, 1)}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    out["hbm_read_gbs"] = round(best(lambda: ha.probe_read(src, sink), 10) / 1e9, 1)
+    out["hbm_copy_gbs"] = round(best(lambda: ha.probe_copy(src, dst), 10) / 1e9, 1)
+    out["hbm_copy_nontemporal_gbs"] = round(best(lambda: ha.probe_copy(src, dst, nontemporal=True), 10) / 1e9, 1)
+    del src, dst
+    out["how"] = (f"probe kernels: {blocks} x 256-thread blocks of 32x32x16 bf16 MFMA chains ({iters} rounds); "
+                  "1 GiB read, copy and non-temporal copy, 10 back-to-back launches; best of 3 after a warm-up")
+    return out
+
+
+def annotate(line, peaks, telemetry):
+    """Add the achievable peaks, the roofline's fraction of them and the telemetry
+    to a bench line (in place)."""
+    line["achievable"] = peaks
+    line["telemetry"] = telemetry
+    r = line.get("roofline")
+    if peaks and r:
+        if r.get("bound") == "mfma":
+            ach = peaks.get("mfma_bf16_tflops")
+        else:
+            ach = max(peaks.get("hbm_read_gbs", 0), peaks.get("hbm_copy_gbs", 0),
+                      peaks.get("hbm_copy_nontemporal_gbs", 0)) or None
+        if ach:
+            r["achievable_peak"] = ach
+            r["frac_of_achievable"] = round(r["achieved"] / ach, 4)
+    return line
 
 
 def measured_traffic(label: str):
@@ -290,7 +481,12 @@ def run_block(args, w):
         "stage_ms": {k: round(v, 3) for k, v in stage.items()},
         "projections": gemm,
     }
-    print(json.dumps(line), flush=True)
+    tele = None if args.no_telemetry else sample_telemetry(step, dev)
+    peaks = None if args.no_peaks else achievable_peaks(dev)
+    if peaks:
+        for k in ("proj_in", "proj_out"):
+            gemm[f"{k}_frac_of_achievable"] = round(gemm[f"{k}_tflops"] / peaks["mfma_bf16_tflops"], 4)
+    print(json.dumps(annotate(line, peaks, tele)), flush=True)
 
 
 def run_train(args, w):
@@ -392,7 +588,9 @@ def run_train(args, w):
         "backward_ms": {k: round(v, 3) for k, v in bwd.items()},
         "linear_backward_hbm_gbs_min_bytes": round(9 * BH * w.N * w.d * 2 / (lin_bwd_ms / 1e3) / 1e9, 1),
     }
-    print(json.dumps(line), flush=True)
+    tele = None if args.no_telemetry else sample_telemetry(step, dev)
+    peaks = None if args.no_peaks else achievable_peaks(dev)
+    print(json.dumps(annotate(line, peaks, tele)), flush=True)
 
 
 def run_stack(args, w):
@@ -480,7 +678,9 @@ def run_stack(args, w):
         "block_ms": round(ms_per_step / nb, 3),
         "mix_ms": round(mix_ms, 3),
     }
-    print(json.dumps(line), flush=True)
+    tele = None if args.no_telemetry else sample_telemetry(step, dev)
+    peaks = None if args.no_peaks else achievable_peaks(dev)
+    print(json.dumps(annotate(line, peaks, tele)), flush=True)
 
 
 def main():
@@ -501,6 +701,10 @@ def main():
                     help="the hybrid group (default), the attention block around it, one training "
                          "step of the group (forward and backward), or a stack of AttnRes-routed blocks")
     ap.add_argument("--blocks", type=int, default=4, help="blocks in --mode stack")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the clock and power sampling (about 2.5 s of untimed steps after the timed ones)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probes (MFMA loop, HBM streams) after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -644,6 +848,8 @@ def main():
         extra["allsoftmax_group_ms"] = round(soft_ms, 3)
         extra["hybrid_speedup_vs_allsoftmax"] = round(soft_ms / ms_per_step, 3)
 
+    tele = None if args.no_telemetry else sample_telemetry(step, dev)
+    peaks = None if args.no_peaks else achievable_peaks(dev)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -670,7 +876,7 @@ def main():
         "cpu_baseline": cpu,
         **extra,
     }
-    print(json.dumps(line), flush=True)
+    print(json.dumps(annotate(line, peaks, tele)), flush=True)
 
 
 if __name__ == "__main__":

@@ -2,7 +2,8 @@
 libhybrid_attn.so.
 
 The functions below only marshal torch tensors (device memory) and the current
-HIP stream into the C ABI of include/hybrid_attn.h; every step of the
+HIP stream into the C ABI of include/hybrid_attn.h (and the measurement probes
+of include/ha_probe.h); every step of the
 computation runs in the library's HIP kernels.  Outputs and the workspace are
 allocated with torch when the caller does not pass them.
 """
@@ -36,6 +37,9 @@ __all__ = [
     "hybrid_attn_proj_out",
     "hybrid_attn_block",
     "block_workspace_bytes",
+    "probe_mfma",
+    "probe_read",
+    "probe_copy",
     "LAYER_KINDS",
 ]
 
@@ -401,3 +405,45 @@ def hybrid_attn_block_routed(x, summaries, w_route, W_in4, W_out4, heads, x_out=
                                                 _dtype_code(x), _ptr(workspace), nbytes, _stream(stream)),
            "hybrid_attn_block_routed")
     return x_out
+
+
+def _stream_buffer(name, t):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    _on_current_device(name, t)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.numel() * t.element_size()
+
+
+def _sink(sink):
+    if sink is None:
+        return torch.empty(1, dtype=torch.float32, device=torch.cuda.current_device())
+    _like("sink", sink, (1,), torch.float32, torch.device("cuda", torch.cuda.current_device()))
+    return sink
+
+
+def probe_mfma(blocks: int, iters: int, sink=None, stream=None) -> float:
+    """Enqueue the MFMA throughput probe; returns the flop count it performs."""
+    sink = _sink(sink)
+    _check(_lib.load().hybrid_attn_probe_mfma(blocks, iters, _ptr(sink), _stream(stream)), "hybrid_attn_probe_mfma")
+    return float(_lib.load().hybrid_attn_probe_mfma_flops(blocks, iters))
+
+
+def probe_read(src, sink=None, stream=None) -> int:
+    """Enqueue the HBM read probe over all of `src`; returns the bytes read."""
+    nbytes = _stream_buffer("src", src)
+    sink = _sink(sink)
+    _check(_lib.load().hybrid_attn_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "hybrid_attn_probe_read")
+    return nbytes
+
+
+def probe_copy(src, dst, nontemporal: bool = False, stream=None) -> int:
+    """Enqueue the HBM copy probe src -> dst (same byte size); returns the bytes
+    moved (read plus written)."""
+    nbytes = _stream_buffer("src", src)
+    if _stream_buffer("dst", dst) != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _check(_lib.load().hybrid_attn_probe_copy(_ptr(src), _ptr(dst), nbytes, int(bool(nontemporal)), _stream(stream)),
+           "hybrid_attn_probe_copy")
+    return 2 * nbytes

@@ -1,4 +1,5 @@
-"""ctypes declaration of libhybrid_attn.so (the C ABI in include/hybrid_attn.h).
+"""ctypes declaration of libhybrid_attn.so (the C ABI in include/hybrid_attn.h and
+the measurement probes in include/ha_probe.h).
 
 Loading is lazy so that the package can be imported to build the library; any
 call into the library raises if it has not been built.  There is no fallback
@@ -10,7 +11,8 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libhybrid_attn.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "hybrid_attn.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADER = os.path.join(INCLUDE, "hybrid_attn.h")
 
 HA_BF16, HA_F32 = 0, 1
 HA_OK, HA_EINVAL, HA_EUNSUPPORTED, HA_EALIGN, HA_EWORKSPACE, HA_EHIP = 0, -1, -2, -3, -4, -5
@@ -43,6 +45,10 @@ SIGNATURES = {
     "hybrid_attn_proj_out": (_i, [_p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_block_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),
     "hybrid_attn_block": (_i, [_p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),
+    "hybrid_attn_probe_mfma_flops": (ctypes.c_double, [_i, _i]),
+    "hybrid_attn_probe_mfma": (_i, [_i, _i, _p, _p]),
+    "hybrid_attn_probe_read": (_i, [_p, _sz, _p, _p]),
+    "hybrid_attn_probe_copy": (_i, [_p, _p, _sz, _i, _p]),
 }
 
 _lib = None
@@ -65,8 +71,12 @@ def load() -> ctypes.CDLL:
     return _lib
 
 
-def header_functions(path: str = HEADER) -> list:
-    """Names of the functions include/hybrid_attn.h declares (HA_API ...)."""
-    with open(path) as f:
-        text = f.read()
-    return re.findall(r"HA_API\s+[\w\s\*]+?\b(hybrid_attn_\w+)\s*\(", text)
+def header_functions(paths=None) -> list:
+    """Names of the functions the headers under include/ declare (HA_API ...)."""
+    if paths is None:
+        paths = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    names = []
+    for path in paths:
+        with open(path) as f:
+            names += re.findall(r"HA_API\s+[\w\s\*]+?\b(hybrid_attn_\w+)\s*\(", f.read())
+    return names

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "../../include/ha_probe.h"
 #include "../../include/hybrid_attn.h"
 #include "ha_launch.h"
 
@@ -583,6 +584,29 @@ HA_API int hybrid_attn_group_schedule(int kinds[4]) {
   static const int schedule[4] = {0, 0, 0, 1};
   memcpy(kinds, schedule, sizeof(schedule));
   return HA_OK;
+}
+
+HA_API double hybrid_attn_probe_mfma_flops(int blocks, int iters) {
+  if (blocks < 1 || blocks > HA_PROBE_MAX_BLOCKS || iters < 1 || iters > HA_PROBE_MAX_ITERS) return 0.0;
+  return ha::probe_mfma_flops(blocks, iters);
+}
+
+HA_API int hybrid_attn_probe_mfma(int blocks, int iters, float* sink, hipStream_t stream) {
+  if (sink == nullptr || blocks < 1 || blocks > HA_PROBE_MAX_BLOCKS || iters < 1 || iters > HA_PROBE_MAX_ITERS)
+    return HA_EINVAL;
+  return hip_status(ha::launch_probe_mfma(blocks, iters, sink, stream));
+}
+
+HA_API int hybrid_attn_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream) {
+  if (src == nullptr || sink == nullptr) return HA_EINVAL;
+  if (misaligned(src) || bytes % 16 != 0) return HA_EALIGN;
+  return hip_status(ha::launch_probe_read(src, bytes, sink, stream));
+}
+
+HA_API int hybrid_attn_probe_copy(const void* src, void* dst, size_t bytes, int nontemporal, hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || overlaps(src, bytes, dst, bytes)) return HA_EINVAL;
+  if (misaligned(src) || misaligned(dst) || bytes % 16 != 0) return HA_EALIGN;
+  return hip_status(ha::launch_probe_copy(src, dst, bytes, nontemporal != 0, stream));
 }
 
 }  // extern "C"

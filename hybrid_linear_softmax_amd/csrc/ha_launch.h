@@ -87,4 +87,10 @@ hipError_t launch_proj_in(bool bf16, const void* x, const void* W_in, void* Q, v
 hipError_t launch_proj_out(bool bf16, const void* O, const void* W_out, const void* x, void* x_out,
                            int64_t B, int64_t H, int64_t N, int d, hipStream_t s);
 
+// Achievable-peak probes (see probe.hip).
+double probe_mfma_flops(int blocks, int iters);
+hipError_t launch_probe_mfma(int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, bool nontemporal, hipStream_t s);
+
 }  // namespace ha

@@ -265,3 +265,23 @@ def test_binding_rejects_host_tensors():
         ha.hybrid_attn_linear(t, t, t, t)
     with pytest.raises(ValueError, match="device tensor"):
         ha.hybrid_attn_proj_in(torch.zeros((1, 8, 128), dtype=torch.bfloat16), torch.zeros((512, 128)), 2)
+
+
+def test_probe_errors(lib):
+    SRC, DST, SINK = GB * 50, GB * 51, GB * 52
+    flops = lib.hybrid_attn_probe_mfma_flops
+    assert flops(1, 1) == 4 * 4 * 2 * 32 * 32 * 16
+    assert flops(2048, 65536) == 2048 * 65536 * flops(1, 1)
+    assert flops(0, 1) == 0.0 and flops(1, 0) == 0.0 and flops(1 << 21, 1) == 0.0 and flops(1, (1 << 24) + 1) == 0.0
+    mfma = lib.hybrid_attn_probe_mfma
+    assert mfma(0, 1, SINK, None) == EINVAL and mfma(1, 0, SINK, None) == EINVAL
+    assert mfma((1 << 20) + 1, 1, SINK, None) == EINVAL and mfma(1, 1, None, None) == EINVAL
+    read = lib.hybrid_attn_probe_read
+    assert read(None, 1024, SINK, None) == EINVAL and read(SRC, 1024, None, None) == EINVAL
+    assert read(SRC + 8, 1024, SINK, None) == EALIGN and read(SRC, 1000, SINK, None) == EALIGN
+    assert read(SRC, 0, SINK, None) == OK                      # nothing enqueued
+    copy = lib.hybrid_attn_probe_copy
+    assert copy(None, DST, 1024, 0, None) == EINVAL and copy(SRC, None, 1024, 0, None) == EINVAL
+    assert copy(SRC, SRC + 512, 1024, 0, None) == EINVAL       # ranges overlap
+    assert copy(SRC, DST + 8, 1024, 1, None) == EALIGN and copy(SRC, DST, 1000, 0, None) == EALIGN
+    assert copy(SRC, DST, 0, 0, None) == OK

@@ -76,3 +76,42 @@ def test_cpu_baseline_sampler_on_a_tiny_workload():
     # more rows than the sequence: every row, once
     r = bench.cpu_baseline(w, x, rows_sampled=10_000, lin_heads=9)
     assert "300 of 300" in r["sample"] and "3 of 3 heads" in r["sample"]
+
+
+def test_telemetry_summary_and_absence():
+    # (metrics timestamp, clock MHz, power W): the first sample may predate the
+    # window and repeats of a timestamp are stale, so both are dropped
+    s = bench.summarize_telemetry([(1, 127, 250.0), (1, 127, 250.0), (2, 2400, 900.0), (2, 2400, 900.0),
+                                   (3, 2300, None), (4, None, 1000.0)])
+    assert s["gfx_clock_mhz"] == {"median": 2350.0, "min": 2300, "max": 2400}
+    assert s["socket_power_w"] == {"median": 950.0, "min": 900.0, "max": 1000.0}
+    assert s["fresh_samples"] == 3
+    # without timestamps (the fallback queries) every sample after the first counts
+    s = bench.summarize_telemetry([(None, 10, 1.0), (None, 20, 2.0), (None, 30, 3.0)])
+    assert s["gfx_clock_mhz"]["median"] == 25.0 and s["fresh_samples"] == 2
+    assert bench.summarize_telemetry([]) is None
+    assert bench.summarize_telemetry([(1, 2400, 900.0)]) is None
+    assert bench.summarize_telemetry([(1, 2400, 900.0), (1, 2400, 900.0)]) is None
+    # where amdsmi has no device (as on a host without the driver) nothing is
+    # sampled and the line carries null
+    t = bench.Telemetry(0, period_s=0.001)
+    with t:
+        pass
+    if not t.available:
+        assert t.summary() is None
+        assert bench.sample_telemetry(lambda: None, types.SimpleNamespace(index=0), seconds=0.0) is None
+
+
+def test_annotate_adds_fraction_of_achievable():
+    peaks = {"mfma_bf16_tflops": 2000.0, "hbm_read_gbs": 6000.0, "hbm_copy_gbs": 5000.0,
+             "hbm_copy_nontemporal_gbs": 6400.0}
+    line = {"roofline": {"bound": "mfma", "achieved": 1000.0}}
+    bench.annotate(line, peaks, None)
+    assert line["roofline"]["achievable_peak"] == 2000.0 and line["roofline"]["frac_of_achievable"] == 0.5
+    assert line["achievable"] is peaks and line["telemetry"] is None
+    line = {"roofline": {"bound": "hbm", "achieved": 3200.0}}
+    bench.annotate(line, peaks, {"samples": 1})
+    assert line["roofline"]["achievable_peak"] == 6400.0 and line["roofline"]["frac_of_achievable"] == 0.5
+    line = {"roofline": {"bound": "mfma", "achieved": 1.0}}
+    bench.annotate(line, None, None)                 # --no-peaks
+    assert "achievable_peak" not in line["roofline"] and line["achievable"] is None

@@ -1,0 +1,45 @@
+"""The achievable-peak probes (include/ha_probe.h) through the C ABI: the copy
+probe reproduces its source bitwise (ordinary and non-temporal accesses, sizes
+that leave a tail after the four-deep loop), the read and MFMA probes complete,
+and the binding returns the work each call performs."""
+import pytest
+import torch
+
+import hybrid_linear_softmax_amd as ha
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 64 << 20])
+@pytest.mark.parametrize("nontemporal", [False, True])
+def test_copy_probe_is_a_copy(nbytes, nontemporal):
+    say(f"copy probe: {nbytes} bytes, nontemporal={nontemporal}")
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    dst = torch.zeros_like(src)
+    assert ha.probe_copy(src, dst, nontemporal=nontemporal) == 2 * nbytes
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+
+
+def test_read_and_mfma_probes_complete():
+    say("read and MFMA probes")
+    src = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    assert ha.probe_read(src, sink) == 1 << 20
+    assert ha.probe_read(src[:48], sink) == 48
+    flops = ha.probe_mfma(8, 16, sink)
+    assert flops == 8 * 4 * 4 * 16 * 2 * 32 * 32 * 16
+    torch.cuda.synchronize()
+    assert sink.item() == 0.0          # the sinks are written only in cases that cannot occur here
+
+
+def test_probe_binding_checks():
+    a = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="same byte size"):
+        ha.probe_copy(a, torch.empty(32, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ha.HybridAttnError):
+        ha.probe_copy(a[:40], torch.empty(40, dtype=torch.uint8, device="cuda"))   # not a multiple of 16
+    with pytest.raises(ha.HybridAttnError):
+        ha.probe_mfma(0, 1)
