@@ -112,6 +112,10 @@ def test_annotate_adds_fraction_of_achievable():
     line = {"roofline": {"bound": "hbm", "achieved": 3200.0}}
     bench.annotate(line, peaks, {"samples": 1})
     assert line["roofline"]["achievable_peak"] == 6400.0 and line["roofline"]["frac_of_achievable"] == 0.5
+    # the sustained MFMA rate, where measured, is the one a steady kernel meets
+    line = {"roofline": {"bound": "mfma", "achieved": 1000.0}}
+    bench.annotate(line, dict(peaks, mfma_bf16_tflops_sustained=1600.0), None)
+    assert line["roofline"]["achievable_peak"] == 1600.0 and line["roofline"]["frac_of_achievable"] == 0.625
     line = {"roofline": {"bound": "mfma", "achieved": 1.0}}
     bench.annotate(line, None, None)                 # --no-peaks
     assert "achievable_peak" not in line["roofline"] and line["achievable"] is None
