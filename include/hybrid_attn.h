@@ -23,7 +23,9 @@
  * including the workspace.  The library allocates nothing, frees nothing and
  * keeps no state between calls, so calls are reentrant.  All work is enqueued
  * asynchronously on `stream` (0 = the null stream) of the current device; inputs
- * must stay alive and unmodified until the stream has passed the call.
+ * must stay alive and unmodified until the stream has passed the call.  No entry
+ * point allocates, copies, clears memory or synchronises, so each can be
+ * captured into a HIP graph on `stream` and replayed on the same buffers.
  *
  * Errors: every entry point validates its arguments on the host, in the order
  * listed under ha_status, and returns before any HIP call when they are invalid:
