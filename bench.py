@@ -295,13 +295,11 @@ def cpu_baseline(w, x, rows_sampled: int, pattern=None, lin_heads: int = 4):
     same), extrapolated to one whole group.  With a block-sparse pattern the rows
     are whole query blocks and the extrapolation is by query-key pairs."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     import oracle
     from workloads import to_f64
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"],
-                  default=1)
+    threads = _blas_threads()
     lin_heads = max(1, min(lin_heads, w.H))
     t_lin = 0.0
     for hh in range(lin_heads):
@@ -354,18 +352,21 @@ def pattern_pairs(N, offsets, indices, only=None):
     return total
 
 
-def block_cpu_baseline(w, blk, rows_sampled: int):
-    """The oracle timed on a sample of one block: the two projections of
-    `rows_sampled` token rows (rows are independent), the linear layer of one
-    head and `rows_sampled` anchor rows of one head, extrapolated to the block."""
-    import numpy as np
+def _blas_threads():
     from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"], default=1)
+
+
+def _block_oracle_seconds(w, blk, rows_sampled: int):
+    """Oracle seconds for one block, extrapolated from a sample: the two
+    projections of `rows_sampled` token rows (rows are independent), the linear
+    layer of one head and `rows_sampled` anchor rows of one head.  Returns
+    (seconds per block, projection s, linear s, anchor-rows s, rows)."""
+    import numpy as np
 
     import oracle
-    from workloads import to_f64
+    from workloads import layer_inputs_host, to_f64
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"],
-                  default=1)
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(w.N, size=min(rows_sampled, w.N), replace=False))
     x = to_f64(blk["x"][:1, rows])
@@ -375,7 +376,6 @@ def block_cpu_baseline(w, blk, rows_sampled: int):
     oracle.project_out(Q, Wo, x)
     t_proj = time.perf_counter() - t0
     # attention on the projected rows of head 0, scaled to the full sequence
-    from workloads import layer_inputs_host
     att = layer_inputs_host(w, 3, B=1, H=1, N=w.N)
     q, k, v, g = (to_f64(att[n][0, 0]) for n in "QKVG")
     t0 = time.perf_counter()
@@ -386,14 +386,96 @@ def block_cpu_baseline(w, blk, rows_sampled: int):
     t_rows = time.perf_counter() - t0
     heads = w.B * w.H
     t_block = 4 * t_proj * (w.B * w.N / rows.size) + 3 * heads * t_lin + heads * (w.N / rows.size) * t_rows
+    return t_block, t_proj, t_lin, t_rows, rows
+
+
+def block_cpu_baseline(w, blk, rows_sampled: int):
+    """The oracle timed on a sample of one block (see _block_oracle_seconds),
+    extrapolated to the block."""
+    t_block, t_proj, t_lin, t_rows, rows = _block_oracle_seconds(w, blk, rows_sampled)
+    heads = w.B * w.H
     return {
         "value": w.B * w.N / t_block,
         "unit": "tokens/s",
-        "cores": threads,
+        "cores": _blas_threads(),
         "kind": "oracle",
         "sample": (f"float64 numpy oracle: projections of {rows.size} token rows ({t_proj:.2f} s), the linear "
                    f"layer of 1 of {heads} heads ({t_lin:.2f} s) and {rows.size} anchor rows of 1 head "
                    f"({t_rows:.2f} s), extrapolated to 4 sub-layers ({t_block:.0f} s per block)"),
+    }
+
+
+def train_cpu_baseline(w, x, dO4, rows_sampled: int, lin_heads: int = 2):
+    """The oracle timed on a sample of one training step: the linear layer's
+    forward and backward on `lin_heads` whole heads, and the anchor's forward
+    and backward over `rows_sampled` query rows of one head -- the oracle's
+    anchor backward walks query rows against all keys, so each row's share of
+    dQ, dK, dV and dG costs the same -- extrapolated to the step (forward and
+    backward of 3 linear layers and the anchor over every head)."""
+    import numpy as np
+
+    import oracle
+    from workloads import to_f64
+
+    lin_heads = max(1, min(lin_heads, w.H))
+    t_lin = 0.0
+    for hh in range(lin_heads):
+        q, k, v, g = (to_f64(x[n][0, 0, hh]) for n in "QKVG")
+        do = to_f64(dO4[0, 0, hh])
+        t0 = time.perf_counter()
+        oracle.linear_attention(q, k, v, g)
+        oracle.linear_attention_backward(q, k, v, g, do)
+        t_lin += time.perf_counter() - t0
+    t_lin /= lin_heads
+    q, k, v, g = (to_f64(x[n][3, 0, 0]) for n in "QKVG")
+    do = to_f64(dO4[3, 0, 0])
+    rows = np.sort(np.random.default_rng(0).choice(w.N, size=min(rows_sampled, w.N), replace=False))
+    t0 = time.perf_counter()
+    oracle.softmax_attention(q, k, v, g, rows=rows)
+    oracle.softmax_attention_backward(q[rows], k, v, g[rows], do[rows])
+    t_rows = time.perf_counter() - t0
+    heads = w.B * w.H
+    t_step = 3 * heads * t_lin + heads * (w.N / rows.size) * t_rows
+    return {
+        "value": w.B * w.N / t_step,
+        "unit": "tokens/s",
+        "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: linear forward + backward of {lin_heads} of {heads} heads "
+                   f"({t_lin:.2f} s each) and anchor forward + backward over {rows.size} of {w.N} query rows "
+                   f"of 1 head ({t_rows:.2f} s), extrapolated to 3 linear + 1 softmax layers over {heads} heads "
+                   f"({t_step:.0f} s per training step)"),
+    }
+
+
+def stack_cpu_baseline(w, nb, blk, summaries, w_route, rows_sampled: int):
+    """The oracle timed on a sample of the AttnRes stack: one block as in
+    block_cpu_baseline, and the routing mixture of each block (k summaries and
+    the stream, three linear sub-layers each) on `rows_sampled` token rows,
+    extrapolated to `nb` blocks."""
+    import numpy as np
+
+    import oracle
+    from workloads import to_f64
+
+    t_block, _, _, _, rows = _block_oracle_seconds(w, blk, rows_sampled)
+    xr = to_f64(blk["x"][:1, rows])
+    t_mix = 0.0
+    for k in range(nb):
+        cand = np.stack([to_f64(summaries[j][:1, rows]) for j in range(k)] + [xr])
+        wr = to_f64(w_route[k, 0])
+        t0 = time.perf_counter()
+        oracle.attnres_mix(cand, wr)
+        t_mix += 3 * (time.perf_counter() - t0) * (w.B * w.N / rows.size)
+    t_stack = nb * t_block + t_mix
+    return {
+        "value": w.B * w.N / t_stack,
+        "unit": "tokens/s",
+        "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: one block sampled as in the block mode ({t_block:.0f} s extrapolated) "
+                   f"and the routing mixtures of {nb} blocks on {rows.size} token rows ({t_mix:.1f} s "
+                   f"extrapolated), {t_stack:.0f} s per stack of {nb} blocks"),
     }
 
 
@@ -479,7 +561,7 @@ def run_block(args, w):
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = block_cpu_baseline(w, blk, args.cpu_rows or 2048)
+        cpu = block_cpu_baseline(w, blk, args.cpu_rows or 16384)
     line = {
         "metric": "attention block (4 projected sub-layers around the 3:1 group) tokens/s",
         "value": round(M / (ms_per_step / 1e3), 1),
@@ -586,6 +668,10 @@ def run_train(args, w):
         "traffic": None,
     }
     lin_bwd_ms = sum(v for k, v in bwd.items() if k.startswith("bwd_linear")) / 3
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = train_cpu_baseline(w, x, dO4, args.cpu_rows or 16384)
     line = {
         "metric": "hybrid 3:1 group training step (forward + backward) tokens/s",
         "value": round(w.B * w.N / (ms_per_step / 1e3), 1),
@@ -602,7 +688,7 @@ def run_train(args, w):
         "config": {"workload": f"{w.name}_train", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "layers": "linear,linear,linear,softmax", "parallelism": "single-gpu"},
         "roofline": roofline,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "forward_ms": round(fwd_ms, 3),
         "backward_ms": {k: round(v, 3) for k, v in bwd.items()},
         "linear_backward_hbm_gbs_min_bytes": round(9 * BH * w.N * w.d * 2 / (lin_bwd_ms / 1e3) / 1e9, 1),
@@ -669,6 +755,11 @@ def run_stack(args, w):
     torch.cuda.synchronize()
     mix_ms = e0.elapsed_time(e1) / 5
     mix_bytes = (nb + 1) * M * C * 2   # nb candidates read once, h written
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = stack_cpu_baseline(w, nb, {"x": x, "W_in": W_in[0], "W_out": W_out[0]}, summaries, w_route,
+                                 args.cpu_rows or 16384)
     line = {
         "metric": "stack of AttnRes-routed attention blocks tokens/s",
         "value": round(M / (ms_per_step / 1e3), 1),
@@ -693,7 +784,7 @@ def run_stack(args, w):
             "frac": round(mix_bytes / (mix_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": None,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "block_ms": round(ms_per_step / nb, 3),
         "mix_ms": round(mix_ms, 3),
     }
@@ -712,8 +803,8 @@ def main():
                     help="steps of the all-softmax group (4 anchors) for the speedup ratio; 0 skips")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None,
-                    help="softmax rows the oracle baseline samples (default: 32768 for the group, about 10 s "
-                         "of host work; 2048 for --mode block)")
+                    help="query or token rows the oracle baseline samples (default: 32768 for the group, "
+                         "16384 for --mode train, block and stack: about 5-15 s of host work each)")
     ap.add_argument("--anchor", choices=("dense", "lvsa"), default="dense",
                     help="dense softmax anchor (default) or the block-sparse LVSA anchor")
     ap.add_argument("--mode", choices=("group", "block", "train", "stack"), default="group",

@@ -119,3 +119,24 @@ def test_annotate_adds_fraction_of_achievable():
     line = {"roofline": {"bound": "mfma", "achieved": 1.0}}
     bench.annotate(line, None, None)                 # --no-peaks
     assert "achievable_peak" not in line["roofline"] and line["achievable"] is None
+
+
+def test_train_and_stack_cpu_baselines_on_a_tiny_workload():
+    import dataclasses
+
+    from workloads import get
+    w = dataclasses.replace(get("480p"), N=300, H=2, d=16)
+    g = torch.Generator().manual_seed(1)
+    x = {n: torch.randn((4, 1, w.H, w.N, w.d), generator=g) for n in "QKVG"}
+    dO4 = torch.randn((4, 1, w.H, w.N, w.d), generator=g)
+    r = bench.train_cpu_baseline(w, x, dO4, rows_sampled=64)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert "64 of 300 query rows" in r["sample"] and "2 of 2 heads" in r["sample"]
+    C, nb = w.H * w.d, 3
+    blk = {"x": torch.randn((1, w.N, C), generator=g), "W_in": torch.randn((4, 4 * C, C), generator=g),
+           "W_out": torch.randn((4, C, C), generator=g)}
+    summaries = torch.randn((nb, 1, w.N, C), generator=g)
+    w_route = torch.randn((nb, 4, C), generator=g)
+    r = bench.stack_cpu_baseline(w, nb, blk, summaries, w_route, rows_sampled=50)
+    assert r["kind"] == "oracle" and r["value"] > 0
+    assert "3 blocks on 50 token rows" in r["sample"]
