@@ -7,19 +7,30 @@
 // Both are dense contractions over C, run on the bf16 MFMA with float32
 // accumulation.
 //
-// bf16 kernel: one block = 256 output features x 256 tokens, 8 waves (2 along
-// features x 4 along tokens, 128 x 64 each), K in steps of 64.
+// bf16 kernel: one block = 256 output features x 256 tokens, 8 waves, each
+// owning 128 features x 64 tokens of the output, K in steps of 32.
 //  * the product is taken transposed, out^T = W x^T: the MFMA A operand is a
-//    weight row, the B operand a token row, both contiguous along C, so both
-//    LDS tiles are read the same way, and a lane's accumulator holds four
-//    consecutive output features of one token -- an 8-byte store in either
-//    epilogue (the head scatter of proj_in, the residual add of proj_out);
+//    weight row, the B operand a token row, both contiguous along C, and a
+//    lane's accumulator holds four consecutive output features of one token --
+//    an 8-byte store in either epilogue (the head scatter of proj_in, the
+//    residual add of proj_out);
+//  * two-group ping-pong: waves 0-3 and 4-7 (one of each per SIMD) alternate,
+//    between block barriers, a compute phase -- 16 MFMAs on operands already in
+//    registers -- and a memory phase -- the LDS reads of the operands of their
+//    next K step and the loads of a K step three ahead -- so that in every phase
+//    one wave per SIMD keeps the matrix core busy.  Each group runs a loop of its
+//    own (phases in opposite order), with no role branch inside it;
+//  * K tiles come straight from global memory into LDS (global_load_lds, 16
+//    bytes per lane, no registers): a ring of four 32 KB stages, rows of 64 bytes
+//    whose 16-byte chunks are XOR-swizzled by row so that the fragment reads of
+//    32 consecutive rows hit distinct banks; group 0 loads the weight half of a
+//    stage, group 1 the token half.  Waits on those loads are explicit (the
+//    compiler does not track them), placed before the barrier that precedes a
+//    stage's first read;
 //  * proj_out reads its token rows straight out of O's [B, H, N, d] layout: a
-//    64-wide K step lies inside one head, so a row is 128 contiguous bytes;
+//    32-wide K step lies inside one head, so a row is 64 contiguous bytes;
 //  * tiles past M tokens or the last feature clamp their load rows to the last
 //    valid row (valid memory, results never stored), so no load is predicated;
-//  * global loads of the next K step are in flight during the MFMAs of the
-//    current one; LDS is double buffered with one barrier per step;
 //  * tiles are ordered in groups of 4 token tiles x all feature tiles and the
 //    order is split into 8 contiguous ranges, one per XCD, so the blocks that
 //    run together on one XCD share token rows and weight rows in its L2.
@@ -32,9 +43,24 @@ namespace {
 
 constexpr int kTF = 256;   // output features per block
 constexpr int kTM = 256;   // tokens per block
-constexpr int kTK = 64;    // K per step
+constexpr int kTK = 32;    // K per step
 constexpr int kGroupM = 4; // token tiles per ordering group
-constexpr int kLP = kTK + 8;  // LDS pitch (elements) of a 64-wide row
+constexpr int kStages = 4; // LDS ring
+constexpr int kStage = (kTF + kTM) * kTK;  // elements per stage: weight rows, then token rows
+
+// chunk swizzle of a stage row: 16-byte chunk c of row r sits in slot c ^ swz(r)
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt vmcnt(n) with the LDS and export counters left at their maxima
+#define HA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// block barrier after this wave's LDS accesses have completed; the sched and
+// asm barriers keep the phases' instructions on their side of it
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 struct ProjShape {
   int64_t M;      // tokens B * N
@@ -43,6 +69,7 @@ struct ProjShape {
   int64_t N;      // tokens per batch item
   int64_t H;
   int d;
+  int lgd;        // log2(d): d is 64 or 128
   int64_t nt_f, nt_m, total;
 };
 
@@ -63,57 +90,73 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
                                                     bf16_t* out0, bf16_t* __restrict__ out1,
                                                     bf16_t* __restrict__ out2, bf16_t* __restrict__ out3,
                                                     const bf16_t* resid, ProjShape p) {
-  __shared__ __attribute__((aligned(16))) bf16_t sW[2][kTF * kLP];
-  __shared__ __attribute__((aligned(16))) bf16_t sX[2][kTM * kLP];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[kStages * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const int wf = wave >> 2;  // 128-feature half
+  const int wf = wave >> 2;  // group: 128-feature half, and the half of each stage it loads
   const int wt = wave & 3;   // 64-token quarter
   int64_t tf, tm;
   tile_of(xcd_remap(blockIdx.x, p.total), p, tf, tm);
   const int64_t f0 = tf * kTF, m0 = tm * kTM;
+  const int nk = static_cast<int>(p.K / kTK);
 
-  // rows this thread loads: r = (tid + 512 i) / 8, 16-byte chunk kc = tid % 8
-  const int kc = tid & 7;
-  int64_t xrow[4], wrow[4];
+  // Loads: wave (wf, wt) fills rows 64 wt + 16 j .. + 15 (j < 4) of its group's
+  // half of a stage, one 1 KB global_load_lds each; lane L fills row
+  // 64 wt + 16 j + L / 4, slot L % 4, with the row's chunk (L % 4) ^ swz(row).
+  const bf16_t* src[4];
+  int ldst[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 64 * i;
-    const int64_t m = min(m0 + r, p.M - 1);
-    if (MODE == 0) {
-      xrow[i] = m * p.K;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 64 * wt + 16 * j + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(256 * wf + r);
+    if (wf == 0) {
+      src[j] = W + min(f0 + r, p.Nf - 1) * p.K + 8 * chunk;
     } else {
-      const int64_t b = m / p.N, n = m - b * p.N;
-      xrow[i] = (b * p.H * p.N + n) * p.d;
+      const int64_t m = min(m0 + r, p.M - 1);
+      if (MODE == 0) {
+        src[j] = X + m * p.K + 8 * chunk;
+      } else {
+        const int64_t b = m / p.N, n = m - b * p.N;
+        src[j] = X + (b * p.H * p.N + n) * p.d + 8 * chunk;
+      }
     }
-    wrow[i] = min(f0 + r, p.Nf - 1) * p.K;
+    ldst[j] = (256 * wf + 64 * wt + 16 * j) * kTK;
   }
-  auto xcol = [&](int64_t k0) -> int64_t {
-    if (MODE == 0) return k0 + 8 * kc;
-    return (k0 / p.d) * p.N * p.d + (k0 % p.d) + 8 * kc;
+  // element offset of K step t: weights and proj_in tokens are contiguous in K;
+  // proj_out tokens jump from head to head every d features
+  auto k_off = [&](int t) -> int64_t {
+    const int64_t k0 = static_cast<int64_t>(t) * kTK;
+    if (MODE == 0 || wf == 0) return k0;
+    return (k0 >> p.lgd) * p.N * p.d + (k0 & (p.d - 1));
   };
-  u32x4 xr[4], wr[4];
-  auto load = [&](int64_t k0) {
-    const int64_t xc = xcol(k0), wc = k0 + 8 * kc;
+  auto load_stage = [&](int t) {
+    bf16_t* base = lds + (t % kStages) * kStage;
+    const int64_t off = k_off(t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xr[i] = *reinterpret_cast<const u32x4*>(X + xrow[i] + xc);
-      wr[i] = *reinterpret_cast<const u32x4*>(W + wrow[i] + wc);
+    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(src[j] + off, base + ldst[j], 16, 0, 0);
+  };
+  bf16x8 a[4][2], bx[2][2];
+  auto read_operands = [&](int t) {
+    const bf16_t* base = lds + (t % kStages) * kStage;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = 2 * kk + h;
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi) {
+        const int row = 128 * wf + 32 * fi + l32;
+        a[fi][kk] = *reinterpret_cast<const bf16x8*>(base + row * kTK + 8 * (c ^ swz(row)));
+      }
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int row = 256 + 64 * wt + 32 * ti + l32;
+        bx[ti][kk] = *reinterpret_cast<const bf16x8*>(base + row * kTK + 8 * (c ^ swz(row)));
+      }
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 64 * i;
-      *reinterpret_cast<u32x4*>(&sX[buf][r * kLP + 8 * kc]) = xr[i];
-      *reinterpret_cast<u32x4*>(&sW[buf][r * kLP + 8 * kc]) = wr[i];
-    }
-  };
-
   f32x16 acc[4][2];
 #pragma unroll
   for (int fi = 0; fi < 4; ++fi)
@@ -121,64 +164,106 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fi][ti][r] = 0.f;
-
-  const int64_t nk = p.K / kTK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int buf = static_cast<int>(ks & 1);
-    // unconditional (the last step re-reads its own slice into the idle
-    // buffer): a conditional load keeps the prefetch registers in scratch
-    load(min(ks + 1, nk - 1) * kTK);
-    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the MFMAs
+  auto compute = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < kTK / 16; ++kk) {
-      bf16x8 a[4], bx[2];
-#pragma unroll
-      for (int fi = 0; fi < 4; ++fi)
-        a[fi] = *reinterpret_cast<const bf16x8*>(&sW[buf][(128 * wf + 32 * fi + l32) * kLP + 16 * kk + 8 * h]);
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-        bx[ti] = *reinterpret_cast<const bf16x8*>(&sX[buf][(64 * wt + 32 * ti + l32) * kLP + 16 * kk + 8 * h]);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
-          acc[fi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fi], bx[ti], acc[fi][ti], 0, 0, 0);
+          acc[fi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fi][kk], bx[ti][kk], acc[fi][ti], 0, 0, 0);
+  };
+
+  // Step t is loaded in phase pair t - 3 (the prologue loads steps 0-2) and read
+  // by group 0 in the second phase of pair t - 1, by group 1 in the first phase
+  // of pair t.  Before the barrier that precedes group 0's read, every wave waits
+  // until at most its loads of later steps are outstanding (4 per step).
+  const int pre = min(nk, 3);
+  for (int t = 0; t < pre; ++t) load_stage(t);
+  if (pre == 3) {
+    HA_WAIT_VMCNT(8);
+  } else if (pre == 2) {
+    HA_WAIT_VMCNT(4);
+  } else {
+    HA_WAIT_VMCNT(0);
+  }
+  phase_barrier();
+  if (wf == 0) {
+    read_operands(0);
+    for (int s = 0; s < nk; ++s) {
+      compute();
+      if (s + 2 < nk) {
+        HA_WAIT_VMCNT(4);  // step s + 2 may stay in flight
+      } else {
+        HA_WAIT_VMCNT(0);
+      }
+      phase_barrier();
+      if (s + 1 < nk) read_operands(s + 1);
+      if (s + 3 < nk) load_stage(s + 3);
+      phase_barrier();
     }
-    store(buf ^ 1);
-    __syncthreads();
+  } else {
+    for (int s = 0; s < nk; ++s) {
+      read_operands(s);
+      if (s + 3 < nk) {
+        load_stage(s + 3);
+        HA_WAIT_VMCNT(8);  // steps s + 2 and s + 3 may stay in flight
+      } else {
+        HA_WAIT_VMCNT(0);
+      }
+      phase_barrier();
+      compute();
+      phase_barrier();
+    }
   }
 
-  // epilogue: lane holds features f .. f+3 of token m for each (fi, ti, g)
+  // epilogue: lane holds features f .. f+3 of token m for each (fi, ti, g).  A
+  // 32-aligned run of features lies inside one head of one tensor (C and d are
+  // multiples of 32), so each fi needs one 32-bit division by C.
   const int64_t C = MODE == 0 ? p.K : p.Nf;
+  bf16_t* dst_fi[4];
+  int64_t col_fi[4];
+#pragma unroll
+  for (int fi = 0; fi < 4; ++fi) {
+    const int64_t fb = f0 + 128 * wf + 32 * fi;
+    if (MODE == 0) {
+      const uint32_t t = static_cast<uint32_t>(fb) / static_cast<uint32_t>(C);
+      const int64_t fc = fb - static_cast<int64_t>(t) * C;
+      dst_fi[fi] = t == 0 ? out0 : t == 1 ? out1 : t == 2 ? out2 : out3;
+      col_fi[fi] = (fc >> p.lgd) * p.N * p.d + (fc & (p.d - 1));  // head offset + feature in head
+    } else {
+      dst_fi[fi] = out0;
+      col_fi[fi] = fb;
+    }
+  }
 #pragma unroll
   for (int ti = 0; ti < 2; ++ti) {
     const int64_t m = m0 + 64 * wt + 32 * ti + l32;
     if (m >= p.M) continue;
-    const int64_t b = m / p.N, n = m - b * p.N;
+    int64_t row;  // element offset of token m's row
+    if (MODE == 0) {
+      const int64_t b = m / p.N, n = m - b * p.N;
+      row = (b * p.H * p.N + n) * p.d;
+    } else {
+      row = m * C;
+    }
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi)
+    for (int fi = 0; fi < 4; ++fi) {
+      if (f0 + 128 * wf + 32 * fi >= p.Nf) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t f = f0 + 128 * wf + 32 * fi + 8 * g + 4 * h;
-        if (f >= p.Nf) continue;
         const float v0 = acc[fi][ti][4 * g + 0], v1 = acc[fi][ti][4 * g + 1];
         const float v2 = acc[fi][ti][4 * g + 2], v3 = acc[fi][ti][4 * g + 3];
+        const int64_t off = row + col_fi[fi] + 8 * g + 4 * h;
         if (MODE == 0) {
-          const int64_t t = f / C, fc = f - t * C;
-          const int64_t hh = fc / p.d, e = fc - hh * p.d;
-          bf16_t* dst = t == 0 ? out0 : t == 1 ? out1 : t == 2 ? out2 : out3;
-          *reinterpret_cast<uint2*>(dst + ((b * p.H + hh) * p.N + n) * p.d + e) =
-              make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+          *reinterpret_cast<uint2*>(dst_fi[fi] + off) = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
         } else {
-          const int64_t off = m * C + f;
           const uint2 rv = *reinterpret_cast<const uint2*>(resid + off);
           *reinterpret_cast<uint2*>(out0 + off) =
               make_uint2(pack_bf16(bf_lo(rv.x) + v0, bf_hi(rv.x) + v1), pack_bf16(bf_lo(rv.y) + v2, bf_hi(rv.y) + v3));
         }
       }
+    }
   }
 }
 
@@ -246,6 +331,7 @@ ProjShape shape(int64_t B, int64_t H, int64_t N, int d, bool in) {
   p.N = N;
   p.H = H;
   p.d = d;
+  p.lgd = d == 128 ? 7 : 6;
   p.nt_f = (p.Nf + kTF - 1) / kTF;
   p.nt_m = (p.M + kTM - 1) / kTM;
   p.total = p.nt_f * p.nt_m;
