@@ -341,6 +341,32 @@ def cpu_baseline(w, x, rows_sampled: int, pattern=None, lin_heads: int = 4):
     }
 
 
+def linear_kernel_split(B, H, N, d, r1_ms, layer_ms):
+    """Per-kernel figures of one linear layer from two event timings: R1 (the
+    state reduction, both passes, timed through hybrid_attn_kv_state) and the
+    whole layer; R2 (the apply) is the difference, so it carries the gap between
+    the layer's launches (rocprofv3's per-kernel durations are the finer
+    figure).  Algorithmic bytes and flops
+    per (token, head): R1 reads K and V (4d bytes) for 2d^2 + d flops, R2 reads
+    Q and G and writes O (6d bytes) for 2d^2 + 6d flops (bf16 I/O)."""
+    th = B * H * N
+    r2_ms = max(layer_ms - r1_ms, 1e-9)
+    r1_bytes, r2_bytes = th * 4 * d, th * 6 * d
+    r1_flop, r2_flop = th * (2 * d * d + d), th * (2 * d * d + 6 * d)
+    gbs = lambda b, ms: b / (ms / 1e3) / 1e9   # noqa: E731
+    tfs = lambda f, ms: f / (ms / 1e3) / 1e12  # noqa: E731
+    return {
+        "r1_state_ms": round(r1_ms, 4),
+        "r1_hbm_gbs": round(gbs(r1_bytes, r1_ms), 1),
+        "r1_hbm_frac": round(gbs(r1_bytes, r1_ms) / HBM_PEAK_GBS, 4),
+        "r1_mfma_frac": round(tfs(r1_flop, r1_ms) / MFMA_BF16_PEAK_TFLOPS, 4),
+        "r2_apply_ms": round(r2_ms, 4),
+        "r2_hbm_gbs": round(gbs(r2_bytes, r2_ms), 1),
+        "r2_hbm_frac": round(gbs(r2_bytes, r2_ms) / HBM_PEAK_GBS, 4),
+        "r2_mfma_frac": round(tfs(r2_flop, r2_ms) / MFMA_BF16_PEAK_TFLOPS, 4),
+    }
+
+
 def pattern_pairs(N, offsets, indices, only=None):
     """Query-key pairs a block pattern keeps (valid keys only, set semantics)."""
     nkb = -(-N // 64)
@@ -927,6 +953,27 @@ def main():
         "linear_layer_hbm_gbs": round(lin_bytes / (lin_ms / 1e3) / 1e9, 1),
     }
 
+    # per-kernel split of one linear layer (untimed for value): R1 through the
+    # state-reduction entry point, the layer itself, R2 = the difference
+    Sst = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
+    zst = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+
+    def mean_ms(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    r1_ms = mean_ms(lambda: ha.hybrid_attn_kv_state(x["K"][0], x["V"][0], Sst, zst, workspace=ws))
+    lay_ms = mean_ms(lambda: ha.hybrid_attn_linear(x["Q"][0], x["K"][0], x["V"][0], x["G"][0], O4[0], workspace=ws))
+    extra["linear_kernels"] = linear_kernel_split(w.B, w.H, w.N, w.d, r1_ms, lay_ms)
+    del Sst, zst
     if sparse:
         extra["pattern_density"] = round(pairs / (w.N * w.N), 5)
         extra["anchor_pairs"] = pairs

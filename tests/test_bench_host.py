@@ -140,3 +140,15 @@ def test_train_and_stack_cpu_baselines_on_a_tiny_workload():
     r = bench.stack_cpu_baseline(w, nb, blk, summaries, w_route, rows_sampled=50)
     assert r["kind"] == "oracle" and r["value"] > 0
     assert "3 blocks on 50 token rows" in r["sample"]
+
+
+def test_linear_kernel_split_arithmetic():
+    # 720p/5s shape: R1 reads K, V (0.929 GB), R2 reads Q, G and writes O (1.393 GB)
+    k = bench.linear_kernel_split(1, 24, 75600, 128, r1_ms=0.2, layer_ms=0.45)
+    th = 24 * 75600
+    assert k["r2_apply_ms"] == 0.25
+    assert abs(k["r1_hbm_gbs"] - th * 512 / 0.2e-3 / 1e9) < 0.1
+    assert abs(k["r2_hbm_gbs"] - th * 768 / 0.25e-3 / 1e9) < 0.1
+    assert abs(k["r1_hbm_frac"] - k["r1_hbm_gbs"] / 8000.0) < 1e-4
+    assert abs(k["r1_mfma_frac"] - th * (2 * 128 * 128 + 128) / 0.2e-3 / 1e12 / 2500.0) < 1e-4
+    assert abs(k["r2_mfma_frac"] - th * (2 * 128 * 128 + 6 * 128) / 0.25e-3 / 1e12 / 2500.0) < 1e-4
