@@ -55,6 +55,19 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _check_no_undefined_kernels(lib: str) -> None:
+    """A kernel whose host launch stub the compiler failed to emit shows up as
+    an undefined symbol of the library's own namespace; refuse such a library
+    (it would only fail later, when loaded)."""
+    nm = shutil.which("nm") or shutil.which("llvm-nm")
+    if nm is None:
+        return
+    res = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    missing = [line.split()[-1] for line in res.stdout.splitlines() if "_ZN2ha" in line]
+    if missing:
+        raise RuntimeError(f"{lib} has undefined symbols of its own code: {missing[:4]}")
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
@@ -64,6 +77,7 @@ def build(verbose: bool = True) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stderr}")
+    _check_no_undefined_kernels(tmp)
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

@@ -54,6 +54,13 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 // s_waitcnt vmcnt(n) with the LDS and export counters left at their maxima
 #define HA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+// 16 bytes per lane from global memory straight into LDS at dst + 16 lane (dst
+// wave-uniform).  Kept out of the kernel's lambdas: a target builtin inside a
+// lambda can make the host compilation drop the kernel's launch stub.
+__device__ __forceinline__ void global_to_lds16(const bf16_t* src, bf16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 // block barrier after this wave's LDS accesses have completed; the sched and
 // asm barriers keep the phases' instructions on their side of it
 __device__ __forceinline__ void phase_barrier() {
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
     bf16_t* base = lds + (t % kStages) * kStage;
     const int64_t off = k_off(t);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(src[j] + off, base + ldst[j], 16, 0, 0);
+    for (int j = 0; j < 4; ++j) global_to_lds16(src[j] + off, base + ldst[j]);
   };
   bf16x8 a[4][2], bx[2][2];
   auto read_operands = [&](int t) {
