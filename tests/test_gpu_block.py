@@ -153,3 +153,33 @@ def test_720p5s_stages_sampled():
     assert torch.equal(out, y)
     del t, Q, K, V, G, O, out, y
     torch.cuda.empty_cache()
+
+
+def test_14b_b2_projections_sampled():
+    # the widest shape of the workloads (C = 5120: 160 K steps of 32 per tile,
+    # 80 feature tiles in proj_in), both batch items
+    w = get("14b_b2")
+    C = w.H * w.d
+    say(f"projections 14b_b2: B={w.B} N={w.N} C={C}: generating inputs")
+    t = block_inputs_device(w, DEV, layers=1)
+    rows = sample_rows(w.N, n_rand=96, seed=4)
+    x = t["x"]
+    Q, K, V, G = ha.hybrid_attn_proj_in(x, t["W_in"][0], w.H)
+    torch.cuda.synchronize()
+    xr = to_f64(x[:, rows])
+    ref = oracle.project_in(xr, to_f64(t["W_in"][0]), w.H)
+    for name, g, r in zip("QKVG", (Q, K, V, G), ref):
+        e = rel_err(to_f64(g[:, :, rows]), r)
+        assert e < TOL["bf16"], (name, e)
+    del K, V, G
+    say("  proj_in sampled rows ok")
+    gen = torch.Generator(device=DEV).manual_seed(6)
+    O = (torch.randn((w.B, w.H, w.N, w.d), generator=gen, device=DEV) * 0.05).to(x.dtype)
+    x1 = ha.hybrid_attn_proj_out(O, t["W_out"][0], x)
+    torch.cuda.synchronize()
+    ref1 = oracle.project_out(to_f64(O[:, :, rows]), to_f64(t["W_out"][0]), xr)
+    e = rel_err(to_f64(x1[:, rows]), ref1)
+    say(f"  proj_out sampled rows: {e:.2e}")
+    assert e < TOL["bf16"]
+    del t, Q, O, x1
+    torch.cuda.empty_cache()
