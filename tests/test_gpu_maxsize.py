@@ -121,3 +121,23 @@ def test_blocksparse_anchor_at_max_n(inputs):
     e = rel_err(got, ref)
     say(f"  block-sparse N=2^23: {rows.size} rows, max rel err {e:.2e}")
     assert e < TOL["bf16"]
+
+
+def test_linear_and_anchor_at_max_n_d64():
+    # the other head size at the largest sequence: one bf16 head of d = 64 is
+    # 2^30 bytes; the anchor's lse held to the same derived bound
+    w = dataclasses.replace(get("720p5s"), name="maxn_d64", H=1, N=MAX_N, d=64)
+    say(f"max-size inputs: B=1 H=1 N={MAX_N} d=64 bf16")
+    x = layer_inputs_device(w, 0, "cuda")
+    torch.cuda.synchronize()
+    k, v = to_f64(x["K"][0, 0]), to_f64(x["V"][0, 0])
+    rows = sample_rows(MAX_N, n_rand=24, seed=9)
+    O = ha.hybrid_attn_linear(x["Q"], x["K"], x["V"], x["G"])
+    torch.cuda.synchronize()
+    ref = oracle.linear_attention(to_f64(x["Q"][0, 0][rows]), k, v, to_f64(x["G"][0, 0][rows]))
+    e = rel_err(to_f64(O[0, 0][rows]), ref)
+    say(f"  linear N=2^23 d=64: {rows.size} rows, max rel err {e:.2e}")
+    assert e < TOL["bf16"]
+    del O
+    say("  anchor N=2^23 d=64 (about 15 s on the GPU)")
+    _check_anchor_lse(x, k, v, rows, "bf16", "anchor N=2^23 d=64")
