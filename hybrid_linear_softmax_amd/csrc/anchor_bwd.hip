@@ -316,10 +316,13 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
       preD = q < N ? Dv[bh * N + q] : 0.f;
     }
   };
+  // row-major writes: in instruction j a thread writes row 4 sm + (j + rot) % 4
+  // of its four, so that 8 (or 16) neighbouring lanes, which differ in sm,
+  // cover distinct LDS banks; the transposed writes need the rows in order and
+  // go first
+  const int rot = ((sm >> 2) + 2 * ((sm >> 1) & 1)) & 3;
   auto commit = [&]() {
     if (loader) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&dst_row[(4 * sm + j) * KP + 8 * sfg]) = pre[j];
       const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&pre[0]);
       const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&pre[1]);
       const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&pre[2]);
@@ -332,6 +335,16 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
         *reinterpret_cast<uint2*>(&dst_t[(8 * sfg + 2 * p + 1) * TP + pos]) =
             make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u), __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
       }
+      if (rot & 1) {
+        const uint4 t0 = pre[0];
+        pre[0] = pre[1]; pre[1] = pre[2]; pre[2] = pre[3]; pre[3] = t0;
+      }
+      if (rot & 2) {
+        const uint4 t0 = pre[0], t1 = pre[1];
+        pre[0] = pre[2]; pre[1] = pre[3]; pre[2] = t0; pre[3] = t1;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&dst_row[(4 * sm + ((j + rot) & 3)) * KP + 8 * sfg]) = pre[j];
     }
     if (tid < BQ) {
       sL[tid] = preL;
