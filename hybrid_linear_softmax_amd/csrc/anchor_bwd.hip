@@ -363,18 +363,24 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+    // S and dP with each k-slice's fragments read one slice ahead
+    bf16x8 fq[2], fa[2], fk[2], fv[2];
+    auto frag = [&](int st, int b) {
+      fq[b] = *reinterpret_cast<const bf16x8*>(&sQ[(32 * t + l32) * KP + 16 * st + 8 * h]);
+      fa[b] = *reinterpret_cast<const bf16x8*>(&sA[(32 * t + l32) * KP + 16 * st + 8 * h]);
+      fk[b] = *reinterpret_cast<const bf16x8*>(&sKw[(32 * kw + l32) * KP + 16 * st + 8 * h]);
+      fv[b] = *reinterpret_cast<const bf16x8*>(&sVw[(32 * kw + l32) * KP + 16 * st + 8 * h]);
+    };
+    frag(0, 0);
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sQ[(32 * t + l32) * KP + 16 * st + 8 * h]);
-      const bf16x8 aa = *reinterpret_cast<const bf16x8*>(&sA[(32 * t + l32) * KP + 16 * st + 8 * h]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&sKw[(32 * kw + l32) * KP + 16 * st + 8 * h]);
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&sVw[(32 * kw + l32) * KP + 16 * st + 8 * h]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, dp, 0, 0, 0);
+      if (st + 1 < KS) frag(st + 1, (st + 1) & 1);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[st & 1], fk[st & 1], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st & 1], fv[st & 1], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     float p[16], ds[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    auto probs = [&](int g) {  // P and dS of accumulator rows 4 g .. 4 g + 3
       const float4 L4 = *reinterpret_cast<const float4*>(&sL[32 * t + 8 * g + 4 * h]);
       const float4 D4 = *reinterpret_cast<const float4*>(&sD[32 * t + 8 * g + 4 * h]);
       const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
@@ -385,7 +391,11 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
         p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -Lr[j]));
         ds[r] = p[r] * (dp[r] - Dr[j]);
       }
-    }
+    };
+    // the second half's P and dS are computed in the shadow of the first
+    // half's dV/dK MFMAs (pinned there by the empty asm statements)
+    probs(0);
+    probs(1);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       uint4 pk, dk4;
@@ -400,6 +410,12 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
         const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&sQt[(32 * rb + l32) * TP + 32 * t + 16 * tt + 8 * h]);
         dv[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pf, dv[rb], 0, 0, 0);
         dk[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf, dk[rb], 0, 0, 0);
+        if (tt == 0 && rb < 2) {
+          probs(2 + rb);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(p[8 + 4 * rb + u]), "+v"(ds[8 + 4 * rb + u]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
