@@ -2,8 +2,9 @@
 one bf16 head of d = 128 is exactly 2^31 bytes and the anchor's 32-bit buffer
 offsets and record counts sit at their limit), one head, checked against the
 oracle on sampled query rows (rows are independent, so each is an exact check).
-The anchor's backward at this length would run for minutes and is not run
-here; its kernels use the same offset arithmetic as the forward.
+The anchor's backward at this length would run for minutes; it runs at half
+of it (2^22 tokens, one head), with dQ and dG exact on sampled rows and dK, dV
+through identities that hold at any length.
 
 Sums over millions of keys are where fp32 accumulation breaks down: with the
 near-flat logits of these inputs every probability is close to one, and a
@@ -141,3 +142,61 @@ def test_linear_and_anchor_at_max_n_d64():
     del O
     say("  anchor N=2^23 d=64 (about 15 s on the GPU)")
     _check_anchor_lse(x, k, v, rows, "bf16", "anchor N=2^23 d=64")
+
+
+BWD_N = 1 << 22
+
+
+def _sum_rows_f64(t, chunk=1 << 20):
+    """Column sums of a [N, d] device tensor, widened exactly to float64."""
+    return sum(to_f64(t[r:r + chunk]).sum(axis=0) for r in range(0, t.shape[0], chunk))
+
+
+@pytest.mark.timeout(300)
+def test_anchor_backward_at_4m():
+    w = dataclasses.replace(get("720p5s"), name="bwd4m", H=1, N=BWD_N)
+    say(f"backward inputs: B=1 H=1 N={BWD_N} d=128 bf16")
+    x = layer_inputs_device(w, 3, "cuda")
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    dO = torch.randn((1, 1, BWD_N, w.d), generator=gen, device="cuda").to(torch.bfloat16)
+    say("  anchor forward with lse and backward at N=2^22 (about 40 s on the GPU)")
+    O, lse = ha.hybrid_attn_softmax_lse(x["Q"], x["K"], x["V"], x["G"])
+    dQ, dK, dV, dG = ha.hybrid_attn_softmax_backward(x["Q"], x["K"], x["V"], x["G"], O, dO, lse)
+    torch.cuda.synchronize()
+    del O, lse
+    # dQ, dG: exact on sampled query rows (a row's gradient needs its own row
+    # and every key)
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(BWD_N - 8, BWD_N), rng.choice(BWD_N, 16, replace=False)]))
+    k, v = to_f64(x["K"][0, 0]), to_f64(x["V"][0, 0])
+    q, g, do = (to_f64(t[0, 0][rows]) for t in (x["Q"], x["G"], dO))
+    rq, rg = oracle.softmax_attention_backward_rows(q, k, v, g, do, np.arange(rows.size))
+    del k, v
+    eq, eg = rel_err(to_f64(dQ[0, 0][rows]), rq), rel_err(to_f64(dG[0, 0][rows]), rg)
+    say(f"  dQ, dG on {rows.size} rows: {eq:.2e}, {eg:.2e}")
+    assert eq < TOL["bf16"] and eg < TOL["bf16"]
+    # dV: every query's probabilities sum to one over the keys, so the key sum
+    # of dV = P^T da is the query sum of da = dO * sigmoid(G).  Bound per
+    # feature: the bf16 roundings of da, of each probability and of the lse
+    # each move a term by at most 2^-9 of |da| (3 x 2^-9 sum |da|), the bf16
+    # store of dV by 2^-9 sum |dV|; doubled for fp32 accumulation
+    sd, sad = np.zeros(w.d), np.zeros(w.d)
+    chunk = 1 << 20
+    for r in range(0, BWD_N, chunk):
+        da = to_f64(dO[0, 0][r:r + chunk]) * oracle.sigmoid(to_f64(x["G"][0, 0][r:r + chunk]))
+        sd += da.sum(axis=0)
+        sad += np.abs(da).sum(axis=0)
+    sv = _sum_rows_f64(dV[0, 0])
+    sav = sum(np.abs(to_f64(dV[0, 0][r:r + chunk])).sum(axis=0) for r in range(0, BWD_N, chunk))
+    ev = np.abs(sv - sd)
+    bound = 2.0 * (3 * 2.0 ** -9 * sad + 2.0 ** -9 * sav)
+    say(f"  dV key sum vs da query sum: max {ev.max():.3e} (bound {bound.min():.3e})")
+    assert np.all(ev <= bound)
+    # dK: a common shift of every key leaves the anchor unchanged, so the key
+    # gradients sum to zero (relative to their total size)
+    sk = _sum_rows_f64(dK[0, 0])
+    sak = sum(np.abs(to_f64(dK[0, 0][r:r + chunk])).sum(axis=0) for r in range(0, BWD_N, chunk))
+    say(f"  dK key sum: {np.abs(sk).max():.3e} of {sak.max():.3e}")
+    assert np.abs(sk).max() < 2e-2 * sak.max()
+    for t in (dQ, dK, dV, dG):
+        assert torch.isfinite(t).all()
