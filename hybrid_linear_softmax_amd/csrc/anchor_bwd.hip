@@ -93,22 +93,48 @@ __global__ __launch_bounds__(256) void sm_bwd_pre(const T* __restrict__ O, const
 }
 
 // ------------------------------------------------------------------ bf16 dQ
-// 4 waves x 32 queries per block, 64-key steps.  Per step: S^T and dP^T
+// 8 waves x 32 queries per block, 64-key steps.  Per step: S^T and dP^T
 // (keys x queries) on the 32x32x16 MFMA with the wave's Q and da rows as
-// register-resident B operands, then dQ^T += K^T dS^T.
+// register-resident B operands, then dQ^T += K^T dS^T.  K and V tiles come
+// straight from global memory into a double-buffered LDS ring (the next tile
+// loads during the current step's MFMAs), in unpadded rows whose 16-byte
+// chunk c sits in slot c ^ (row mod chunks per row).
+
+// 16 bytes per lane from a buffer straight into LDS at dst + 16 lane (dst
+// wave-uniform).  A device function: a target builtin inside a kernel lambda
+// can make the host compilation drop the kernel's launch stub.
+__device__ __forceinline__ void dq_tile_to_lds16(__amdgpu_buffer_rsrc_t r, bf16_t* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, static_cast<int>(voff), 0, 0, 0);
+}
+
+// barrier that waits for this wave's LDS accesses only: the direct tile loads
+// in flight (counted by vmcnt) are waited for explicitly where they are needed
+__device__ __forceinline__ void dq_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+__global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                                                       const bf16_t* __restrict__ V, const bf16_t* __restrict__ da,
                                                       const float* __restrict__ lse, const float* __restrict__ Dv,
                                                       bf16_t* __restrict__ dQ, int64_t N, int64_t qblocks,
                                                       float c) {
-  constexpr int NT = 256, BK = 64;
-  constexpr int KP = D + 8, TP = BK + 8, FG = D / 8;
-  constexpr int KCH = BK * FG / NT;     // 16-byte chunks per thread per tile
+  constexpr int NT = 512, BK = 64, BQ = 256;
+  constexpr int TP = BK + 8, FG = D / 8;
   constexpr int KS = D / 16, RB = D / 32;
-  constexpr int TSUB = (BK / 4) * FG;   // 4-key x 8-feature sub-tiles of the K^T transpose
-  __shared__ __attribute__((aligned(16))) bf16_t sK[BK * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[BK * KP];
+  constexpr int TSUB = (BK / 4) * FG;    // 4-key x 8-feature sub-tiles of the K^T transpose
+  constexpr int TILE = BK * D;           // elements of one K or V tile
+  constexpr int RPL = 64 / FG;           // rows per 1 KB load
+  constexpr int NLD = TILE / 512 / (NT / 64);  // 1 KB loads per wave per tile
+  static_assert(NLD * (NT / 64) * 512 == TILE, "tile split over the waves");
+  // two buffers as separate arrays, so that the loads into one are seen not to
+  // alias the reads of the other
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[TILE];
   __shared__ __attribute__((aligned(16))) bf16_t sKt[D * TP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -117,7 +143,7 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
   // XCDs, which measured faster here than one head per XCD (xcd_remap)
   const int64_t id = blockIdx.x;
   const int64_t bh = id / qblocks;
-  const int64_t qrow = (id % qblocks) * 128 + 32 * wave + l32;
+  const int64_t qrow = (id % qblocks) * BQ + 32 * wave + l32;
   const int64_t base = bh * N * D;
   const uint32_t head_bytes = static_cast<uint32_t>(N * D * 2);
   const __amdgpu_buffer_rsrc_t rK =
@@ -140,23 +166,39 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[rb][r] = 0.f;
 
-  const int64_t nkb = (N + BK - 1) / BK;
-  for (int64_t kb = 0; kb < nkb; ++kb) {
-    const int64_t k0 = kb * BK;
-    __syncthreads();
+  // load j of this wave fills rows RPL (NLD wave + j) .. + RPL - 1 of a tile;
+  // lane L fills row RPL (NLD wave + j) + L / FG, slot L % FG, with the row's
+  // chunk (L % FG) ^ (row mod FG).  Rows past N read zeros.
+  uint32_t voff[NLD];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + NT * i;
-      const uint32_t off = static_cast<uint32_t>((k0 + cidx / FG) * (D * 2) + (cidx % FG) * 16);
-      *reinterpret_cast<uint4*>(&sK[(cidx / FG) * KP + 8 * (cidx % FG)]) = buffer_load16(rK, off);
-      *reinterpret_cast<uint4*>(&sV[(cidx / FG) * KP + 8 * (cidx % FG)]) = buffer_load16(rV, off);
+  for (int j = 0; j < NLD; ++j) {
+    const int row = RPL * (NLD * wave + j) + lane / FG;
+    voff[j] = static_cast<uint32_t>(row * (D * 2) + (((lane % FG) ^ (row & (FG - 1))) * 16));
+  }
+  auto load_tile = [&](int64_t kb, bf16_t* tK, bf16_t* tV) {
+    const uint32_t t0 = static_cast<uint32_t>(kb * BK * (D * 2));
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      dq_tile_to_lds16(rK, tK + 512 * (NLD * wave + j), t0 + voff[j]);
+      dq_tile_to_lds16(rV, tV + 512 * (NLD * wave + j), t0 + voff[j]);
     }
-    __syncthreads();
+  };
+  const int sw = l32 & (FG - 1);   // chunk swizzle of this lane's fragment rows
+
+  const int64_t nkb = (N + BK - 1) / BK;
+  load_tile(0, sK0, sV0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 is in LDS
+  __syncthreads();
+  auto step = [&](int64_t kb, const bf16_t* sK, const bf16_t* sV, bf16_t* nK, bf16_t* nV) {
+    const int64_t k0 = kb * BK;
     if (tid < TSUB) {   // K^T: 4 keys x 8 features per thread
       const int fg = tid / (BK / 4), m = tid % (BK / 4);
       uint4 r[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const uint4*>(&sK[(4 * m + j) * KP + 8 * fg]);
+      for (int j = 0; j < 4; ++j) {
+        const int row = 4 * m + j;
+        r[j] = *reinterpret_cast<const uint4*>(&sK[row * D + 8 * (fg ^ (row & (FG - 1)))]);
+      }
       const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&r[0]);
       const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&r[1]);
       const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&r[2]);
@@ -170,7 +212,9 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
             make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u), __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
       }
     }
-    __syncthreads();
+    // the next tile loads into the other buffer (last read in the previous step)
+    if (kb + 1 < nkb) load_tile(kb + 1, nK, nV);
+    dq_barrier();
     // valid keys of this block, less this lane's accumulator row offset 4 h
     const int limh = static_cast<int>(min((int64_t)BK, N - k0)) - 4 * h;
 #pragma unroll
@@ -180,8 +224,9 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[(32 * t + l32) * KP + 16 * st + 8 * h]);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[(32 * t + l32) * KP + 16 * st + 8 * h]);
+        const int off = (32 * t + l32) * D + 8 * ((2 * st + h) ^ sw);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[off]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[off]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, af[st], dp, 0, 0, 0);
       }
@@ -204,6 +249,12 @@ __global__ __launch_bounds__(256) void sm_bwd_dq_bf16(const bf16_t* __restrict__
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile is in LDS
+    dq_barrier();                        // and everyone is done with this one and K^T
+  };
+  for (int64_t kb = 0; kb < nkb; kb += 2) {
+    step(kb, sK0, sV0, sK1, sV1);
+    if (kb + 1 < nkb) step(kb + 1, sK1, sV1, sK0, sV0);
   }
   if (qrow < N) {
     const float scale = c / kLog2e;
@@ -594,15 +645,15 @@ hipError_t launch_softmax_backward(bool bf16, int d, const void* Q, const void* 
     const bf16_t* k = static_cast<const bf16_t*>(K);
     const bf16_t* v = static_cast<const bf16_t*>(V);
     const bf16_t* a = static_cast<const bf16_t*>(da);
-    const int64_t qb = (N + 127) / 128, tq = BH * qb;
+    const int64_t qb = (N + 255) / 256, tq = BH * qb;
     const int64_t kb = (N + 127) / 128, tk = BH * kb;
     if (d == 128) {
-      sm_bwd_dq_bf16<128><<<dim3(static_cast<unsigned>(tq)), dim3(256), 0, s>>>(q, k, v, a, lse, Dv,
+      sm_bwd_dq_bf16<128><<<dim3(static_cast<unsigned>(tq)), dim3(512), 0, s>>>(q, k, v, a, lse, Dv,
                                                                                  static_cast<bf16_t*>(dQ), N, qb, c);
       sm_bwd_dkv_bf16<128><<<dim3(static_cast<unsigned>(tk)), dim3(512), 0, s>>>(
           q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, c);
     } else {
-      sm_bwd_dq_bf16<64><<<dim3(static_cast<unsigned>(tq)), dim3(256), 0, s>>>(q, k, v, a, lse, Dv,
+      sm_bwd_dq_bf16<64><<<dim3(static_cast<unsigned>(tq)), dim3(512), 0, s>>>(q, k, v, a, lse, Dv,
                                                                                 static_cast<bf16_t*>(dQ), N, qb, c);
       sm_bwd_dkv_bf16<64><<<dim3(static_cast<unsigned>(tk)), dim3(512), 0, s>>>(
           q, k, v, a, lse, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), N, kb, c);
