@@ -222,13 +222,19 @@ __global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      bf16x8 fk[2], fv[2];
+      auto frag = [&](int st, int b) {
+        const int off = (32 * t + l32) * D + 8 * ((2 * st + h) ^ sw);
+        fk[b] = *reinterpret_cast<const bf16x8*>(&sK[off]);
+        fv[b] = *reinterpret_cast<const bf16x8*>(&sV[off]);
+      };
+      frag(0, 0);
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const int off = (32 * t + l32) * D + 8 * ((2 * st + h) ^ sw);
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[off]);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[off]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, af[st], dp, 0, 0, 0);
+        if (st + 1 < KS) frag(st + 1, (st + 1) & 1);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[st & 1], qf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[st & 1], af[st], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       float ds[16];
 #pragma unroll
