@@ -333,6 +333,7 @@ def cpu_baseline(w, x, rows_sampled: int, pattern=None, lin_heads: int = 4):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "host": host_info(),
         "sample": (f"float64 numpy oracle: full linear layer of {lin_heads} of {heads} heads "
                    f"({t_lin:.2f} s each) and "
                    f"{rows.size} of {w.N} {'block-sparse ' if pattern else ''}softmax query rows of 1 head "
@@ -379,8 +380,73 @@ def pattern_pairs(N, offsets, indices, only=None):
 
 
 def _blas_threads():
+    import numpy  # noqa: F401  (loads the BLAS library threadpoolctl inspects)
     from threadpoolctl import threadpool_info
     return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"], default=1)
+
+
+def host_info():
+    """What the CPU baseline ran on: the CPU model (/proc/cpuinfo), the cores
+    this process may use (its affinity mask), and the BLAS library numpy calls
+    with its thread count (the threads the oracle's products actually use)."""
+    import platform
+
+    import numpy  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {
+        "cpu_model": model,
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "blas": ", ".join(sorted({f"{p.get('internal_api')} {p.get('version') or ''} ({p.get('prefix')})".strip()
+                                  for p in blas})) or "none found",
+        "blas_threads": _blas_threads(),
+    }
+
+
+def single_thread_baselines(tiny=None, lin=None, lin_heads: int = 2):
+    """The oracle on one thread: the whole tiny group (fp32 workload, 4 layers)
+    and the 480p linear layer (`lin_heads` whole heads timed, extrapolated to
+    all heads: each head costs the same).  `tiny` / `lin` override the
+    workloads (for tests)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import get, layer_inputs_host, to_f64
+
+    tiny = tiny or get("tiny")
+    lin = lin or get("480p")
+    res = {}
+    with threadpool_limits(limits=1, user_api="blas"):
+        layers = [layer_inputs_host(tiny, l) for l in range(4)]
+        x = {k: np.stack([to_f64(L[k]) for L in layers]) for k in "QKVG"}
+        t0 = time.perf_counter()
+        oracle.group(x["Q"], x["K"], x["V"], x["G"])
+        t = time.perf_counter() - t0
+        res["tiny_group"] = {"seconds": round(t, 4), "tokens_per_s": round(tiny.B * tiny.N / t, 1),
+                             "shape": f"B={tiny.B} H={tiny.H} N={tiny.N} d={tiny.d} fp32, 4 layers"}
+        heads = max(1, min(lin_heads, lin.H))
+        L = layer_inputs_host(lin, 0, B=1, H=heads)
+        q, k, v, g = (to_f64(L[n][0]) for n in "QKVG")
+        t0 = time.perf_counter()
+        for hh in range(heads):
+            oracle.linear_attention(q[hh], k[hh], v[hh], g[hh])
+        t_head = (time.perf_counter() - t0) / heads
+        t_layer = t_head * lin.B * lin.H
+        res["linear_layer_480p"] = {"seconds": round(t_layer, 3), "tokens_per_s": round(lin.B * lin.N / t_layer, 1),
+                                    "sample": f"{heads} of {lin.B * lin.H} heads timed ({t_head:.3f} s each), "
+                                              "extrapolated to the layer"}
+    return res
 
 
 def _block_oracle_seconds(w, blk, rows_sampled: int):
@@ -1011,6 +1077,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, x, args.cpu_rows or 32768, pattern)
+        cpu["single_thread"] = single_thread_baselines()
 
     line = {
         "metric": ("hybrid 3:1 attention group (block-sparse LVSA anchor) tokens/s; % of bf16 MFMA peak"

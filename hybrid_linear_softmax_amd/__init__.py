@@ -7,7 +7,10 @@ of include/ha_probe.h); every step of the
 computation runs in the library's HIP kernels.  Outputs and the workspace are
 allocated with torch when the caller does not pass them.
 """
+import contextlib
 import ctypes
+import functools
+import inspect
 
 import torch
 
@@ -122,6 +125,22 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run an entry point with `stream` (when given) as torch's current stream,
+    so that every output or workspace it allocates belongs to the stream its
+    kernels run on: the caching allocator then reuses a freed workspace only
+    for work ordered after those kernels."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind(*args, **kwargs).arguments.get("stream")
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -136,6 +155,7 @@ def _workspace(B, H, N, d, dtype, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+@_on_stream
 def hybrid_attn_kv_state(K, V, S=None, z=None, workspace=None, stream=None):
     """Float32 state S [B, H, d, d] and normaliser z [B, H, d] of K, V [B, H, N, d]."""
     ref = _tensors(("K", "V"), (K, V), 4)
@@ -149,6 +169,7 @@ def hybrid_attn_kv_state(K, V, S=None, z=None, workspace=None, stream=None):
     return S, z
 
 
+@_on_stream
 def hybrid_attn_linear(Q, K, V, G, O=None, workspace=None, stream=None):
     """One gated linear-attention layer; Q, K, V, G, O: [B, H, N, d]."""
     ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
@@ -161,6 +182,7 @@ def hybrid_attn_linear(Q, K, V, G, O=None, workspace=None, stream=None):
     return O
 
 
+@_on_stream
 def hybrid_attn_softmax(Q, K, V, G, O=None, stream=None):
     """One gated softmax anchor layer; Q, K, V, G, O: [B, H, N, d]."""
     ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
@@ -172,6 +194,7 @@ def hybrid_attn_softmax(Q, K, V, G, O=None, stream=None):
     return O
 
 
+@_on_stream
 def hybrid_attn_softmax_blocksparse(Q, K, V, G, block_offsets, block_indices, O=None, stream=None):
     """Block-sparse gated softmax anchor; Q, K, V, G, O: [B, H, N, d].  The
     pattern is CSR over query blocks of SPARSE_BLOCK_Q rows: int32 device
@@ -197,6 +220,7 @@ def hybrid_attn_softmax_blocksparse(Q, K, V, G, block_offsets, block_indices, O=
     return O
 
 
+@_on_stream
 def hybrid_attn_group(Q4, K4, V4, G4, O4=None, workspace=None, stream=None, events=None):
     """One 3:1 hybrid group over stacked [4, B, H, N, d] tensors.  `events`: an
     optional list of five torch.cuda.Event(enable_timing=True) recorded before
@@ -251,6 +275,7 @@ def block_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfloat16) 
     return int(_lib.load().hybrid_attn_block_workspace_bytes(B, H, N, d, code))
 
 
+@_on_stream
 def hybrid_attn_proj_in(x, W_in, heads, Q=None, K=None, V=None, G=None, stream=None):
     """Q, K, V, G [B, H, N, d] = the four C-wide blocks of x W_in^T split into
     `heads` heads; x: [B, N, C], W_in: [4C, C]."""
@@ -263,6 +288,7 @@ def hybrid_attn_proj_in(x, W_in, heads, Q=None, K=None, V=None, G=None, stream=N
     return tuple(outs)
 
 
+@_on_stream
 def hybrid_attn_proj_out(O, W_out, x, x_out=None, stream=None):
     """x_out = x + concat_heads(O) W_out^T; O: [B, H, N, d], W_out: [C, C],
     x: [B, N, C].  Pass x_out=x to update x in place."""
@@ -279,6 +305,7 @@ def hybrid_attn_proj_out(O, W_out, x, x_out=None, stream=None):
     return x_out
 
 
+@_on_stream
 def hybrid_attn_block(x, W_in4, W_out4, heads, x_out=None, workspace=None, stream=None):
     """The attention block: four sub-layers (linear, linear, linear, softmax),
     each x = x + concat_heads(layer(split(x W_in[l]^T))) W_out[l]^T.  x: [B, N, C],
@@ -310,6 +337,7 @@ def linear_backward_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.
     return int(_lib.load().hybrid_attn_linear_backward_workspace_bytes(B, H, N, d, code))
 
 
+@_on_stream
 def hybrid_attn_linear_backward(Q, K, V, G, dO, grads=None, workspace=None, stream=None):
     """dQ, dK, dV, dG of the gated linear layer for the upstream gradient dO
     (all [B, H, N, d]).  `grads` may hold four preallocated output tensors."""
@@ -325,6 +353,7 @@ def hybrid_attn_linear_backward(Q, K, V, G, dO, grads=None, workspace=None, stre
     return tuple(grads)
 
 
+@_on_stream
 def hybrid_attn_softmax_lse(Q, K, V, G, O=None, lse=None, stream=None):
     """The gated softmax anchor plus the per-row log-sum-exp (float32 [B, H, N]),
     the forward pass whose outputs hybrid_attn_softmax_backward consumes."""
@@ -343,6 +372,7 @@ def softmax_backward_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch
     return int(_lib.load().hybrid_attn_softmax_backward_workspace_bytes(B, H, N, d, code))
 
 
+@_on_stream
 def hybrid_attn_softmax_backward(Q, K, V, G, O, dO, lse, grads=None, workspace=None, stream=None):
     """dQ, dK, dV, dG of the gated softmax anchor; O and lse from
     hybrid_attn_softmax_lse."""
@@ -359,6 +389,7 @@ def hybrid_attn_softmax_backward(Q, K, V, G, O, dO, lse, grads=None, workspace=N
     return tuple(grads)
 
 
+@_on_stream
 def hybrid_attn_attnres_mix(summaries, x, w, h=None, stream=None):
     """AttnRes mixture h [B, N, C] over the candidates summaries [M, B, N, C]
     (M may be 0; pass None) and x, with routing vector w (float32 [C])."""
@@ -389,6 +420,7 @@ def block_routed_workspace_bytes(B: int, H: int, N: int, d: int, dtype=torch.bfl
     return int(_lib.load().hybrid_attn_block_routed_workspace_bytes(B, H, N, d, code))
 
 
+@_on_stream
 def hybrid_attn_block_routed(x, summaries, w_route, W_in4, W_out4, heads, x_out=None, workspace=None, stream=None):
     """hybrid_attn_block with AttnRes routing of `summaries` ([M, B, N, C] or
     None) into the linear sub-layers; w_route float32 [4, C]."""
@@ -423,6 +455,7 @@ def _sink(sink):
     return sink
 
 
+@_on_stream
 def probe_mfma(blocks: int, iters: int, sink=None, stream=None) -> float:
     """Enqueue the MFMA throughput probe; returns the flop count it performs."""
     sink = _sink(sink)
@@ -430,6 +463,7 @@ def probe_mfma(blocks: int, iters: int, sink=None, stream=None) -> float:
     return float(_lib.load().hybrid_attn_probe_mfma_flops(blocks, iters))
 
 
+@_on_stream
 def probe_read(src, sink=None, stream=None) -> int:
     """Enqueue the HBM read probe over all of `src`; returns the bytes read."""
     nbytes = _stream_buffer("src", src)
@@ -438,6 +472,7 @@ def probe_read(src, sink=None, stream=None) -> int:
     return nbytes
 
 
+@_on_stream
 def probe_copy(src, dst, nontemporal: bool = False, stream=None) -> int:
     """Enqueue the HBM copy probe src -> dst (same byte size); returns the bytes
     moved (read plus written)."""

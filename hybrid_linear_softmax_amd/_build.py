@@ -84,5 +84,55 @@ def build(verbose: bool = True) -> str:
     return LIB_PATH
 
 
+# Host-only AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (the C-ABI validation and every launcher's host code; device code is
+# built as usual, with no sanitizer).  Each sanitizer flag reaches the host
+# compilation only; the link is a plain host link with clang++.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime the sanitized library needs (preloaded
+    into the process that loads it)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's AddressSanitizer runtime not found")
+    return path
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Build libhybrid_attn.so with host-side ASan/UBSan into out_dir; returns
+    the library path (load it with asan_runtime() preloaded)."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [hipcc(), *COMMON_FLAGS, *SANITIZE_HOST, "-I", INCLUDE, "-I", CSRC, "-c", *lang,
+               os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, LIB_NAME)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    clang = os.path.join(rocm, "llvm", "bin", "clang++")
+    cmd = [clang, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan", *objs,
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", lib]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{' '.join(cmd)}\n{res.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build()

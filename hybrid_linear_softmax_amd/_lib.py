@@ -10,7 +10,9 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libhybrid_attn.so")
+# HA_LIBRARY names another build of the same library (the host-sanitized test
+# build); by default the in-tree library is loaded.
+LIB_PATH = os.environ.get("HA_LIBRARY") or os.path.join(PKG, "libhybrid_attn.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 HEADER = os.path.join(INCLUDE, "hybrid_attn.h")
 

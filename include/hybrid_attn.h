@@ -56,7 +56,15 @@ extern "C" {
 /* Storage dtype of Q, K, V, G, O.  HA_BF16: bfloat16 I/O, bf16 MFMA products
  * with float32 accumulation, outputs rounded to nearest even.  HA_F32: float32
  * I/O and float32 arithmetic throughout. */
-typedef enum ha_dtype { HA_BF16 = 0, HA_F32 = 1 } ha_dtype;
+/* The two range markers make the enum as wide as int, so that any int a C
+ * caller passes is a valid value of the type (and is rejected by the check
+ * with HA_EUNSUPPORTED) rather than an out-of-range enum value. */
+typedef enum ha_dtype {
+  HA_BF16 = 0,
+  HA_F32 = 1,
+  HA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  HA_DTYPE_RANGE_MAX_ = 2147483647
+} ha_dtype;
 
 /* Status codes, in the order the checks run. */
 typedef enum ha_status {
@@ -113,12 +121,16 @@ HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, cons
 
 /* Block-sparse gated softmax anchor: the anchor above with each query attending
  * only to the keys of the key blocks its query block lists, i.e. the softmax is
- * taken over the union of those blocks' keys.  This is the block-sparse
- * attention of the pages' long-video setting (LongVie Sparse Attention: the
- * review page, section 3, and the summary page, section 03, where the anchor
- * of the 60-second model attends to a window of frames plus periodic global
- * frames).  The pattern, shared by every batch item and head, is in CSR form in
- * device memory:
+ * taken over the union of those blocks' keys.  The SANA-Video 2.0 pages name
+ * sparse attention only as one part of the Sol-Engine inference stack (summary
+ * page, section 04; review page, section 1) without giving its pattern; the
+ * block-structured sets this entry point takes are those of Long Video Sparse
+ * Attention (LVSA explainer page, "LVSA: Training-Free Sparse Attention for
+ * Long Video Diffusion", section 2, Method: each frame attends to a local
+ * window of frames plus a rotating set of global frames under a frame budget)
+ * and of LoSA's frozen per-query-block key-block sets (LoSA article).  The
+ * pattern, shared by every batch item and head, is in CSR form in device
+ * memory:
  *   block_offsets: int32 [ceil(N / HA_SPARSE_BLOCK_Q) + 1], non-decreasing,
  *                  block_offsets[0] = 0, last entry = num_indices;
  *   block_indices: int32 [num_indices]; query block qb lists the key blocks

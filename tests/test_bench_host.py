@@ -152,3 +152,29 @@ def test_linear_kernel_split_arithmetic():
     assert abs(k["r1_hbm_frac"] - k["r1_hbm_gbs"] / 8000.0) < 1e-4
     assert abs(k["r1_mfma_frac"] - th * (2 * 128 * 128 + 128) / 0.2e-3 / 1e12 / 2500.0) < 1e-4
     assert abs(k["r2_mfma_frac"] - th * (2 * 128 * 128 + 6 * 128) / 0.25e-3 / 1e12 / 2500.0) < 1e-4
+
+
+def test_cpu_baseline_records_the_host():
+    w = types.SimpleNamespace(B=1, H=2, N=200, d=16)
+    g = torch.Generator().manual_seed(1)
+    x = {n: torch.randn((4, w.B, w.H, w.N, w.d), generator=g) for n in "QKVG"}
+    r = bench.cpu_baseline(w, x, rows_sampled=32, lin_heads=1)
+    host = r["host"]
+    assert host["affinity_cores"] == len(os.sched_getaffinity(0))
+    assert host["blas_threads"] == r["cores"] >= 1
+    assert isinstance(host["cpu_model"], str) and host["cpu_model"]
+    assert isinstance(host["blas"], str) and host["blas"]
+
+
+def test_single_thread_baselines_on_small_workloads():
+    from workloads import get
+
+    tiny = get("tiny")
+    lin = types.SimpleNamespace(**{**vars(get("480p")), "N": 512, "H": 6})
+    r = bench.single_thread_baselines(tiny=tiny, lin=lin, lin_heads=2)
+    assert r["tiny_group"]["seconds"] > 0 and r["tiny_group"]["tokens_per_s"] > 0
+    assert "N=256" in r["tiny_group"]["shape"]
+    assert r["linear_layer_480p"]["tokens_per_s"] > 0
+    assert "2 of 6 heads" in r["linear_layer_480p"]["sample"]
+    # the BLAS thread limit is lifted again afterwards
+    assert bench._blas_threads() >= 1

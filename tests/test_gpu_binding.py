@@ -87,3 +87,32 @@ def test_block_and_attnres_tensors_are_checked():
         ha.hybrid_attn_attnres_mix(None, x, w[0].to(torch.bfloat16))
     with pytest.raises(ValueError, match="Q:"):
         ha.hybrid_attn_proj_in(x, W_in4[0], H, Q=torch.empty((B, H, N, d + 1), dtype=x.dtype, device="cuda"))
+
+
+def test_side_stream_allocations_belong_to_that_stream():
+    """An entry point called with stream= allocates its workspace and outputs on
+    that stream: a tensor allocated and filled on the current stream right after
+    the call cannot take the workspace's memory while the side stream's kernels
+    still use it, so the result equals the same call on the current stream."""
+    n = 4096
+    g = torch.Generator(device="cuda").manual_seed(2)
+    Q, K, V, G = (torch.randn((1, 4, n, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    ref_lin = ha.hybrid_attn_linear(Q, K, V, G)
+    dO = torch.randn_like(Q)
+    ref_bwd = ha.hybrid_attn_linear_backward(Q, K, V, G, dO)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        # a long kernel first keeps the side stream busy while the current
+        # stream allocates and writes
+        ha.hybrid_attn_softmax(Q, K, V, G, stream=side)
+        out = ha.hybrid_attn_linear(Q, K, V, G, stream=side)
+        grads = ha.hybrid_attn_linear_backward(Q, K, V, G, dO, stream=side)
+        junk = [torch.full((1 << 22,), 7, dtype=torch.uint8, device="cuda") for _ in range(8)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        del junk
+        assert torch.equal(out, ref_lin)
+        for a, b in zip(grads, ref_bwd):
+            assert torch.equal(a, b)
