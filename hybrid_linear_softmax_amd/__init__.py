@@ -28,6 +28,8 @@ __all__ = [
     "SPARSE_BLOCK_K",
     "hybrid_attn_group",
     "hybrid_attn_group_schedule",
+    "hybrid_attn_group_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "hybrid_attn_linear_backward",
     "hybrid_attn_softmax_lse",
     "hybrid_attn_softmax_backward",
@@ -48,6 +50,7 @@ __all__ = [
 
 LAYER_KINDS = {0: "linear", 1: "softmax"}
 SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 256, 64   # HA_SPARSE_BLOCK_Q / HA_SPARSE_BLOCK_K
+NOALLOC_SCRATCH_BYTES = 64 << 20           # HA_NOALLOC_SCRATCH_BYTES
 _DTYPES = {torch.bfloat16: HA_BF16, torch.float32: HA_F32}
 
 
@@ -245,6 +248,22 @@ def hybrid_attn_group(Q4, K4, V4, G4, O4=None, workspace=None, stream=None, even
                 e.record(s)
         arr = (ctypes.c_void_p * 5)(*(e.cuda_event for e in events))
         _check(lib.hybrid_attn_group_timed(*args, arr), "hybrid_attn_group_timed")
+    return O4
+
+
+@_on_stream
+def hybrid_attn_group_noalloc(Q4, K4, V4, G4, O4, stream=None):
+    """hybrid_attn_group with the library's fixed device scratch array as the
+    workspace: nothing is allocated, here or in the library (O4 is the caller's).
+    Calls that overlap on one device share that array and must not be issued."""
+    ref = _tensors(("Q4", "K4", "V4", "G4"), (Q4, K4, V4, G4), 5)
+    L, B, H, N, d = ref.shape
+    if L != 4:
+        raise ValueError(f"a group has 4 layers, got {L}")
+    _like("O4", O4, ref.shape, ref.dtype, ref.device)
+    _check(_lib.load().hybrid_attn_group_noalloc(_ptr(Q4), _ptr(K4), _ptr(V4), _ptr(G4), _ptr(O4), B, H, N, d,
+                                                 _dtype_code(ref), _stream(stream)),
+           "hybrid_attn_group_noalloc")
     return O4
 
 

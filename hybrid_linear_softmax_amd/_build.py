@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libhybrid_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ("api.cpp", "kv_state.hip", "apply.hip", "anchor.hip", "proj.hip", "linear_bwd.hip", "anchor_bwd.hip", "attnres.hip",
-           "probe.hip")
+           "probe.hip", "noalloc.hip")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -35,6 +35,7 @@ SIGNATURES = {
     "hybrid_attn_group_timed": (_i, [_p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p,
                                      ctypes.POINTER(_p)]),
     "hybrid_attn_group_schedule": (_i, [ctypes.POINTER(_i)]),
+    "hybrid_attn_group_noalloc": (_i, [_p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_linear_backward_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),
     "hybrid_attn_linear_backward": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),
     "hybrid_attn_softmax_lse": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),

@@ -157,6 +157,23 @@ HA_API int hybrid_attn_group(const void* Q4, const void* K4, const void* V4, con
                              int B, int H, int64_t N, int d, ha_dtype dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* hybrid_attn_group for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid allocation): the same
+ * computation with the same kernels (outputs bitwise equal to hybrid_attn_group),
+ * its linear layers' workspace taken from a fixed array of
+ * HA_NOALLOC_SCRATCH_BYTES in the library's device memory instead of a caller
+ * buffer.  The library calls no hipMalloc or hipFree here.  Every device keeps
+ * its own array from its first call until the process ends.  All calls on one
+ * device share that device's array, so calls that overlap on one device (other
+ * streams, other threads) race and must not be issued.  Returns HA_EWORKSPACE
+ * when hybrid_attn_workspace_bytes(B, H, N, d, dtype) exceeds
+ * HA_NOALLOC_SCRATCH_BYTES (at d = 128 that holds for B*H up to about 100),
+ * HA_EHIP when the array's device address cannot be obtained, and otherwise
+ * what hybrid_attn_group returns. */
+#define HA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+HA_API int hybrid_attn_group_noalloc(const void* Q4, const void* K4, const void* V4, const void* G4, void* O4,
+                                     int B, int H, int64_t N, int d, ha_dtype dtype, hipStream_t stream);
+
 /* hybrid_attn_group that also records five caller-created events on `stream`:
  * events[0] before layer 0 and events[l + 1] after layer l, so the caller can
  * time each layer of the group with hipEventElapsedTime.  A NULL `events`

@@ -285,3 +285,21 @@ def test_probe_errors(lib):
     assert copy(SRC, SRC + 512, 1024, 0, None) == EINVAL       # ranges overlap
     assert copy(SRC, DST + 8, 1024, 1, None) == EALIGN and copy(SRC, DST, 1000, 0, None) == EALIGN
     assert copy(SRC, DST, 0, 0, None) == OK
+
+
+def test_noalloc_group_limits(lib):
+    """The scratch-array group rejects problems whose workspace exceeds the
+    array before touching the device, and gives the group's own status to
+    invalid or empty problems (nothing to launch)."""
+    na = lib.hybrid_attn_group_noalloc
+    limit = 64 << 20
+    big = (1, 4096, 1000, 128)                      # one chunk per head: 4096 partial states
+    assert lib.hybrid_attn_workspace_bytes(*big, HA_BF16) > limit
+    assert na(Q, K, V, G, O, *big, HA_BF16, None) == EWS
+    assert lib.hybrid_attn_workspace_bytes(1, 24, 75600, 128, HA_BF16) <= limit   # the 720p/5s shape fits
+    assert lib.hybrid_attn_workspace_bytes(2, 40, 75600, 128, HA_BF16) <= limit   # and the 14B batch
+    assert na(Q, K, V, G, O, 1, 2, 100, 96, HA_BF16, None) == EUNSUP
+    assert na(Q, K, V, G, O, 1, 2, -1, 64, HA_BF16, None) == EINVAL
+    assert na(Q, K, V, G, O, 1, 2, 100, 64, 7, None) == EUNSUP
+    assert na(Q, K, V, G, O, 1, 2, 0, 64, HA_BF16, None) == OK      # empty sequence
+    assert na(Q, K, V, G, O, 0, 2, 100, 64, HA_BF16, None) == OK    # no heads
