@@ -173,16 +173,35 @@ def hybrid_attn_kv_state(K, V, S=None, z=None, workspace=None, stream=None):
 
 
 @_on_stream
-def hybrid_attn_linear(Q, K, V, G, O=None, workspace=None, stream=None):
-    """One gated linear-attention layer; Q, K, V, G, O: [B, H, N, d]."""
+def hybrid_attn_linear(Q, K, V, G, O=None, workspace=None, stream=None, events=None):
+    """One gated linear-attention layer; Q, K, V, G, O: [B, H, N, d].  `events`:
+    an optional list of four torch.cuda.Event(enable_timing=True), recorded
+    before pass 1 of the state reduction, after it, after pass 2 and after the
+    apply."""
     ref = _tensors(("Q", "K", "V", "G"), (Q, K, V, G), 4)
     B, H, N, d = ref.shape
     O = _out("O", O, ref.shape, ref.dtype, ref.device)
     ws, nbytes = _workspace(B, H, N, d, ref.dtype, ref.device, workspace)
-    _check(_lib.load().hybrid_attn_linear(_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), B, H, N, d,
-                                          _dtype_code(ref), _ptr(ws), nbytes, _stream(stream)),
-           "hybrid_attn_linear")
+    args = (_ptr(Q), _ptr(K), _ptr(V), _ptr(G), _ptr(O), B, H, N, d, _dtype_code(ref), _ptr(ws), nbytes,
+            _stream(stream))
+    if events is None:
+        _check(_lib.load().hybrid_attn_linear(*args), "hybrid_attn_linear")
+    else:
+        _check(_lib.load().hybrid_attn_linear_timed(*args, _event_array(events, 4, stream)),
+               "hybrid_attn_linear_timed")
     return O
+
+
+def _event_array(events, n, stream):
+    """A C array of the HIP events behind n torch.cuda.Event objects (created,
+    when torch has not yet done so, by a first record on the call's stream)."""
+    if len(events) != n:
+        raise ValueError(f"events: {n} torch.cuda.Event objects expected")
+    s = torch.cuda.current_stream() if stream is None else stream
+    for e in events:
+        if not e.cuda_event:
+            e.record(s)
+    return (ctypes.c_void_p * n)(*(e.cuda_event for e in events))
 
 
 @_on_stream
@@ -240,14 +259,7 @@ def hybrid_attn_group(Q4, K4, V4, G4, O4=None, workspace=None, stream=None, even
     if events is None:
         _check(lib.hybrid_attn_group(*args), "hybrid_attn_group")
     else:
-        if len(events) != 5:
-            raise ValueError("events: five torch.cuda.Event objects expected")
-        s = torch.cuda.current_stream() if stream is None else stream
-        for e in events:          # torch creates the underlying event on first record
-            if not e.cuda_event:
-                e.record(s)
-        arr = (ctypes.c_void_p * 5)(*(e.cuda_event for e in events))
-        _check(lib.hybrid_attn_group_timed(*args, arr), "hybrid_attn_group_timed")
+        _check(lib.hybrid_attn_group_timed(*args, _event_array(events, 5, stream)), "hybrid_attn_group_timed")
     return O4
 
 

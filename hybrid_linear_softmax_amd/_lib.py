@@ -29,6 +29,8 @@ SIGNATURES = {
     "hybrid_attn_workspace_bytes": (_sz, [_i, _i, _i64, _i, _i]),
     "hybrid_attn_kv_state": (_i, [_p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),
     "hybrid_attn_linear": (_i, [_p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),
+    "hybrid_attn_linear_timed": (_i, [_p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p,
+                                      ctypes.POINTER(_p)]),
     "hybrid_attn_softmax": (_i, [_p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p]),
     "hybrid_attn_softmax_blocksparse": (_i, [_p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _p, _i64, _p]),
     "hybrid_attn_group": (_i, [_p, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),

@@ -20,14 +20,17 @@
 //  * K and V are read with buffer loads whose record count is the head's size:
 //    rows past N read as zero without any per-load bounds arithmetic;
 //  * software pipeline: the logit MFMAs of key block j+1 are interleaved, in
-//    one wave's instruction stream, with the softmax of block j, and the PV
-//    MFMAs of block j with the row max of block j+1; K and V tiles are double-
+//    one wave's instruction stream, with the softmax of block j, then the PV
+//    MFMAs of block j run with the next K/V fragments read ahead; K and V tiles are double-
 //    buffered in LDS, K one block ahead of V, one barrier per key block, and
 //    the global loads of the next tiles are issued at the top of the step;
-//  * the running maximum is updated lazily: the output is rescaled only when a
-//    row maximum grows by more than 2^8 in exp2 units (the probabilities stay
-//    below 256, exact enough in fp32 and bf16), which after the first blocks is
-//    almost never;
+//  * the running maximum is updated lazily and without a per-block maximum: a
+//    block's probabilities are computed against the running maximum m, and only
+//    when some lane's sum of them exceeds 2^8 (so that a probability might) is
+//    the block's exact maximum taken, the output and sums rescaled and the
+//    block's probabilities recomputed.  Every probability that reaches the PV
+//    product is therefore below 256 (exact enough in fp32 and bf16); after the
+//    first blocks the slow path is almost never taken;
 //  * row sums are taken over the bf16-rounded probabilities with v_dot2 (two per
 //    instruction), i.e. over exactly the weights the PV product uses.  Each key
 //    block is summed on its own and joins the running sum through compensated
@@ -48,7 +51,7 @@ constexpr int kBc = 64;   // keys per iteration
 static_assert(kBr == kSparseBlockQ && kBc == kSparseBlockK, "sparse pattern blocks are the tile sizes");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyRescale = 8.0f;  // log2 of the largest unrescaled probability
+constexpr float kSumLimit = 256.0f;  // a lane's block sum that triggers the exact rescale
 
 // LDS column of key k (0..63 inside a key block) in the V^T tile.
 __device__ __forceinline__ int vt_pos(int k) {
@@ -191,18 +194,17 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
     return fmaxf(mx, __shfl_xor(mx, 32));
   };
-  auto rescale = [&](float mx) {
-    if (__any((mx - m) * c > kLazyRescale)) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-      m = m_new;
-      lsum *= alpha;
-      lcomp *= alpha;
+  // raise the running maximum to m_new, rescaling what was summed against the
+  // old one (alpha = 1 when it does not move, also while both are -inf)
+  auto rescale_to = [&](float m_new) {
+    const float alpha = m_new == m ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+    m = m_new;
+    lsum *= alpha;
+    lcomp *= alpha;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[rb][r] *= alpha;
-    }
+      for (int r = 0; r < 16; ++r) o[rb][r] *= alpha;
   };
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   // K and V use separate double buffers; K runs one block ahead of V:
@@ -276,20 +278,21 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
   // apply the key limit lim1 of block j+1 (in sparse mode only when it is
   // below 64).  The step is written in the order it should issue: each logit
   // MFMA of block j+1 is followed by two probabilities of block j (exp2, bf16
-  // pack, row-sum dot), each PV MFMA of block j by a slice of block j+1's row
-  // max (the first three also carry the compensated addition of block j's
-  // probability sum), K/V fragments read two MFMAs ahead.  Empty asm
-  // statements that consume each slice's result pin it between its MFMAs: left
-  // alone, the compiler sinks the VALU work to its first use and clusters the
-  // MFMAs.
+  // pack, row-sum dot), the first three PV MFMAs of block j by the compensated
+  // addition of block j's probability sum, K/V fragments read two MFMAs ahead.
+  // Empty asm statements that consume each result pin it between its MFMAs:
+  // left alone, the compiler sinks the VALU work to its first use and clusters
+  // the MFMAs.  Between the two phases, the rescale test on the block sums.
   auto step = [&](int64_t j, int64_t k1, int64_t k2, int lim1, f32x16 (&scur)[2], f32x16 (&snext)[2],
                   auto masked) {
     const int kb = static_cast<int>((j + 1) & 1);
     const int vb = static_cast<int>(j & 1);
     load_k(k2);
     load_v(k1);
-    // (sparse) while every key seen so far was masked, m = -inf: keep p = 0
-    const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
+    // (sparse) while every key seen so far was masked, m = -inf: probabilities
+    // are taken against 0 (masked keys give 0) and the first valid key forces
+    // the exact rescale below
+    float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
     auto kfrag = [&](int i) -> bf16x8 {
       const int t = i & 1, st = i >> 1;
       return *reinterpret_cast<const bf16x8*>(&sK[kb][(32 * t + l32) * KP + 16 * st + 8 * h]);
@@ -306,6 +309,13 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     for (int i = 0; i < 2; ++i) kf[i] = kfrag(i);
     uint32_t pk[16];
     float lblk = 0.f;  // this block's probabilities, before they join lsum
+    auto prob_pair = [&](int pi) {
+      const int e0 = 2 * pi, e1 = e0 + 1;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[e0 >> 4][e0 & 15], c, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[e1 >> 4][e1 & 15], c, -mc));
+      pk[pi] = pack_bf16(p0, p1);
+      lblk = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[pi]), one, lblk, false);
+    };
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int t = i & 1, st = i >> 1;
@@ -314,14 +324,25 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
       snext[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], snext[t], 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int pi = i * PER + u, e0 = 2 * pi, e1 = e0 + 1;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[e0 >> 4][e0 & 15], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[e1 >> 4][e1 & 15], c, -mc));
-        pk[pi] = pack_bf16(p0, p1);
-        lblk = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[pi]), one, lblk, false);
+        const int pi = i * PER + u;
+        prob_pair(pi);
         asm volatile("" : "+v"(pk[pi]), "+v"(lblk));
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // a probability may exceed the limit only if the lane's block sum does (all
+    // are non-negative); then take block j's exact maximum (its logits are
+    // still in scur), rescale and recompute.  (sparse) the first block with a
+    // valid key after masked ones always takes this path, so that m is finite
+    // from then on.
+    bool exact = lblk > kSumLimit;
+    if (SPARSE) exact = exact || (m == -INFINITY && lblk > 0.f);
+    if (__any(exact)) {
+      rescale_to(fmaxf(m, rowmax(scur)));
+      mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
+      lblk = 0.f;
+#pragma unroll
+      for (int pi = 0; pi < 16; ++pi) prob_pair(pi);
     }
     // P^T operands: pf[t][tt] holds keys 32 t + 16 tt + (the accumulator's 8)
     bf16x8 pf[2][2];
@@ -339,33 +360,22 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
       return *reinterpret_cast<const bf16x8*>(&sVt[vb][(32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h]);
     };
     constexpr int NPV = 4 * RB;          // PV MFMAs per block
-    constexpr int PERM = 32 / NPV;       // logits of the row max per PV MFMA
-    static_assert(PERM * NPV == 32 && PERM % 2 == 0, "32 logits per lane and block");
     bf16x8 vf[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) vf[i] = vfrag(i);
     float ky, kt;  // Kahan terms of the block sum, spread over the first PV MFMAs
-    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int rb = i % RB, q = i / RB, t = q >> 1, tt = q & 1;
       const bf16x8 a = vf[i % 2];
       if (i + 2 < NPV) vf[i % 2] = vfrag(i + 2);
       o[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t][tt], o[rb], 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < PERM; u += 2) {
-        const int e0 = i * PERM + u, e1 = e0 + 1;
-        mx = fmaxf(mx, fmaxf(snext[e0 >> 4][e0 & 15], snext[e1 >> 4][e1 & 15]));
-      }
       if (i == 0) { ky = lblk - lcomp; asm volatile("" : "+v"(ky)); }
       if (i == 1) { kt = lsum + ky; asm volatile("" : "+v"(kt)); }
       if (i == 2) { lcomp = (kt - lsum) - ky; lsum = kt; asm volatile("" : "+v"(lcomp), "+v"(lsum)); }
-      asm volatile("" : "+v"(mx));
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
     store_kv(static_cast<int>(j & 1), static_cast<int>((j + 1) & 1));
-    rescale(mx);
     __syncthreads();
   };
   using NoMask = std::integral_constant<bool, false>;

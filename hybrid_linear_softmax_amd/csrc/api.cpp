@@ -70,9 +70,11 @@ int check_workspace(const Problem& p, const void* ws, size_t ws_bytes, const voi
 
 int hip_status(hipError_t e) { return e == hipSuccess ? HA_OK : HA_EHIP; }
 
-// One linear layer on validated arguments.
+// One linear layer on validated arguments.  events (optional, four): recorded
+// before pass 1 of the state reduction, after it, after pass 2, after the apply.
 int run_linear(const Problem& p, const void* Q, const void* K, const void* V, const void* G,
-               void* O, void* ws, hipStream_t s) {
+               void* O, void* ws, hipStream_t s, hipEvent_t const* events = nullptr) {
+  auto mark = [&](int i) { return events == nullptr || hipEventRecord(events[i], s) == hipSuccess; };
   const int d = static_cast<int>(p.d);
   const ha::LinearWs L = ha::linear_ws(p.BH, p.N, d, p.bf16);
   char* w = static_cast<char*>(ws);
@@ -82,12 +84,14 @@ int run_linear(const Problem& p, const void* Q, const void* K, const void* V, co
   uint16_t* hi = reinterpret_cast<uint16_t*>(w + L.St_hi);
   uint16_t* lo = reinterpret_cast<uint16_t*>(w + L.St_lo);
   const ha::KvSplit sp = ha::kv_split(p.BH, p.N);
+  if (!mark(0)) return HA_EHIP;
   hipError_t e = ha::launch_kv_partials(p.bf16, d, K, V, part, p.BH, p.N, sp, s);
-  if (e != hipSuccess) return HA_EHIP;
+  if (e != hipSuccess || !mark(1)) return HA_EHIP;
   e = ha::launch_kv_reduce(p.bf16, d, part, S, z, hi, lo, p.BH, sp.chunks, s);
-  if (e != hipSuccess) return HA_EHIP;
+  if (e != hipSuccess || !mark(2)) return HA_EHIP;
   e = ha::launch_apply(p.bf16, d, Q, G, O, S, z, hi, lo, p.BH, p.N, HA_LINEAR_EPS, s);
-  return hip_status(e);
+  if (e != hipSuccess || !mark(3)) return HA_EHIP;
+  return HA_OK;
 }
 
 // Null, alignment and aliasing checks of inputs and outputs of different
@@ -242,6 +246,26 @@ HA_API int hybrid_attn_linear(const void* Q, const void* K, const void* V, const
   st = check_workspace(p, workspace, workspace_bytes, t, tb, 5);
   if (st != HA_OK) return st;
   return run_linear(p, Q, K, V, G, O, workspace, stream);
+}
+
+HA_API int hybrid_attn_linear_timed(const void* Q, const void* K, const void* V, const void* G, void* O,
+                                    int B, int H, int64_t N, int d, ha_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t const events[4]) {
+  if (events == nullptr) return HA_EINVAL;
+  for (int i = 0; i < 4; ++i)
+    if (events[i] == nullptr) return HA_EINVAL;
+  Problem p;
+  int st = check_shape(B, H, N, d, dtype, &p);
+  if (st != HA_OK) return st;
+  if (p.BH == 0 || p.N == 0) return HA_OK;
+  const void* in[4] = {Q, K, V, G};
+  st = check_buffers(in, 4, p.tensor_bytes, O, p.tensor_bytes);
+  if (st != HA_OK) return st;
+  const void* t[5] = {Q, K, V, G, O};
+  const size_t tb[5] = {p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes, p.tensor_bytes};
+  st = check_workspace(p, workspace, workspace_bytes, t, tb, 5);
+  if (st != HA_OK) return st;
+  return run_linear(p, Q, K, V, G, O, workspace, stream, events);
 }
 
 HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, const void* G, void* O,

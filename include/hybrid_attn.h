@@ -108,6 +108,16 @@ HA_API int hybrid_attn_linear(const void* Q, const void* K, const void* V, const
                               int B, int H, int64_t N, int d, ha_dtype dtype,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* hybrid_attn_linear that also records four caller-created events on `stream`:
+ * events[0] before pass 1 of the state reduction, events[1] after it,
+ * events[2] after pass 2 and events[3] after the apply, so the caller can time
+ * each kernel of the layer with hipEventElapsedTime.  HA_EINVAL for a NULL
+ * array or entry; otherwise exactly hybrid_attn_linear (the same result). */
+HA_API int hybrid_attn_linear_timed(const void* Q, const void* K, const void* V, const void* G, void* O,
+                                    int B, int H, int64_t N, int d, ha_dtype dtype,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t const events[4]);
+
 /* One gated softmax anchor layer (formula above), logit scale 1/sqrt(d).  No
  * workspace.  O must not overlap any input. */
 HA_API int hybrid_attn_softmax(const void* Q, const void* K, const void* V, const void* G, void* O,

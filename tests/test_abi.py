@@ -137,6 +137,13 @@ def test_group_errors(lib):
     assert lib.hybrid_attn_group(*bad, WS, need, None) == EINVAL
     evs = (ctypes.c_void_p * 5)(1, 2, None, 4, 5)
     assert lib.hybrid_attn_group_timed(*args, WS, need, None, evs) == EINVAL
+    # the timed linear layer: a missing event array or entry, then the layer's own checks
+    ev4 = (ctypes.c_void_p * 4)(1, 2, 3, None)
+    assert lib.hybrid_attn_linear_timed(*args, WS, need, None, ev4) == EINVAL
+    assert lib.hybrid_attn_linear_timed(*args, WS, need, None, None) == EINVAL
+    ev4 = (ctypes.c_void_p * 4)(1, 2, 3, 4)
+    assert lib.hybrid_attn_linear_timed(*args, WS, need - 1, None, ev4) == EWS
+    assert lib.hybrid_attn_linear_timed(Q, K, V, G, O, 1, 2, 100, 80, HA_BF16, WS, need, None, ev4) == EUNSUP
     assert lib.hybrid_attn_group(Q, K, V, G, O, 1, 2, 100, 80, HA_BF16, WS, need, None) == EUNSUP
     # the workspace may not overlap any of the stacked tensors, layer 3 included
     assert lib.hybrid_attn_group(*args, O + 3 * layer_bytes, need, None) == EINVAL

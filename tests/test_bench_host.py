@@ -144,9 +144,9 @@ def test_train_and_stack_cpu_baselines_on_a_tiny_workload():
 
 def test_linear_kernel_split_arithmetic():
     # 720p/5s shape: R1 reads K, V (0.929 GB), R2 reads Q, G and writes O (1.393 GB)
-    k = bench.linear_kernel_split(1, 24, 75600, 128, r1_ms=0.2, layer_ms=0.45)
+    k = bench.linear_kernel_split(1, 24, 75600, 128, r1_ms=0.2, reduce_ms=0.015, apply_ms=0.25)
     th = 24 * 75600
-    assert k["r2_apply_ms"] == 0.25
+    assert k["r2_apply_ms"] == 0.25 and k["r1_reduce_ms"] == 0.015
     assert abs(k["r1_hbm_gbs"] - th * 512 / 0.2e-3 / 1e9) < 0.1
     assert abs(k["r2_hbm_gbs"] - th * 768 / 0.25e-3 / 1e9) < 0.1
     assert abs(k["r1_hbm_frac"] - k["r1_hbm_gbs"] / 8000.0) < 1e-4

@@ -144,3 +144,29 @@ def test_720p60s_lvsa_sampled():
         assert e < TOL[w.dtype]
     del x, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_leading_invalid_blocks_then_growing_logits(dtype, d):
+    """Every list starts with entries that name no key (so the running maximum
+    is still -inf when the first valid keys arrive), then valid blocks whose
+    logits grow along the sequence, so that a later block raises the maximum
+    and rescales what the first valid blocks contributed."""
+    N = 1100
+    x = _inputs(dtype, d, 1, 2, N)
+    f = 1.0 if dtype == "f32" else d ** 0.5
+    ramp = torch.linspace(0.5, 4.0, N, device=DEV)[None, None, :, None]
+    x["Q"] = (x["Q"].float() * f).to(x["Q"].dtype)
+    x["K"] = (x["K"].float() * f * ramp).to(x["K"].dtype)
+    nqb, nkb = -(-N // 256), -(-N // 64)
+    lists = [[-1, nkb + 5] + list(range(nkb)) for _ in range(nqb)]
+    offsets = np.cumsum([0] + [len(l) for l in lists]).astype(np.int32)
+    indices = np.asarray([b for l in lists for b in l], dtype=np.int32)
+    say(f"sparse leading invalid blocks {dtype} d={d}")
+    out = _run(x, offsets, indices)
+    _check_full(x, out, offsets, indices, TOL[dtype], f"leading-invalid {dtype} d={d}")
+    # the same sets without the invalid entries: the same output up to rounding
+    off2 = np.arange(nqb + 1, dtype=np.int32) * nkb
+    idx2 = np.tile(np.arange(nkb, dtype=np.int32), nqb)
+    ref_out = _run(x, off2, idx2)
+    assert rel_err(to_f64(out), to_f64(ref_out)) < TOL[dtype]
