@@ -12,8 +12,8 @@ namespace ha {
 // Token split of the linear-state reduction: a pure function of (BH, N), never
 // of the device, so the reduction order (and the result) is reproducible.
 struct KvSplit {
-  int64_t chunk_len;  // tokens per chunk, a multiple of 64
-  int64_t chunks;     // ceil(N / chunk_len), 0 when N == 0
+  int64_t chunks;     // pass-1 blocks (partials) per head; block c takes every
+                      // chunks-th tile starting at tile c; 0 when N == 0
 };
 KvSplit kv_split(int64_t BH, int64_t N);
 
