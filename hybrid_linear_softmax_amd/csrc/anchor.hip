@@ -21,7 +21,8 @@
 //    rows past N read as zero without any per-load bounds arithmetic;
 //  * software pipeline: the logit MFMAs of key block j+1 are interleaved, in
 //    one wave's instruction stream, with the softmax of block j, then the PV
-//    MFMAs of block j run with the next K/V fragments read ahead; K and V tiles are double-
+//    MFMAs of block j run with the next K/V fragments read ahead (the first
+//    phase at raised wave priority); K and V tiles are double-
 //    buffered in LDS, K one block ahead of V, one barrier per key block, and
 //    the global loads of the next tiles are issued at the top of the step;
 //  * the running maximum is updated lazily and without a per-block maximum: a
@@ -289,6 +290,9 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     const int vb = static_cast<int>(j & 1);
     load_k(k2);
     load_v(k1);
+    // the VALU-heavy phase runs at raised wave priority, the PV MFMAs at the
+    // normal one (measured 1-2 % faster at 480p, 720p/5s and 14B)
+    __builtin_amdgcn_s_setprio(2);
     // (sparse) while every key seen so far was masked, m = -inf: probabilities
     // are taken against 0 (masked keys give 0) and the first valid key forces
     // the exact rescale below
@@ -355,6 +359,7 @@ __global__ __launch_bounds__(512, 1) void anchor_bf16(const bf16_t* __restrict__
     if (decltype(masked)::value) {
       if (!SPARSE || lim1 < kBc) mask(snext, lim1);
     }
+    __builtin_amdgcn_s_setprio(0);
     auto vfrag = [&](int i) -> bf16x8 {
       const int rb = i % RB, q = i / RB, t = q >> 1, tt = q & 1;
       return *reinterpret_cast<const bf16x8*>(&sVt[vb][(32 * rb + l32) * VP + 32 * t + 16 * tt + 8 * h]);
