@@ -236,6 +236,20 @@ def achievable_peaks(dev, reps=3):
         torch.cuda.synchronize()
     out["mfma_bf16_tflops_sustained"] = round(flops / (ev[1].elapsed_time(ev[2]) / 1e3) / 1e12, 1)
     out["mfma_sustained_telemetry"] = tele.summary()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ov_iters = 20000
+    def launch_ms(mode, wps):
+        def one():
+            ha.probe_overlap(mode, wps, cus, ov_iters, sink)
+            return 1.0                          # one launch: best() then gives launches per second
+        return 1e3 / best(one)
+
+    times = {(mode, wps): launch_ms(mode, wps)
+             for mode, wps in (("mfma", 1), ("valu", 1), ("both", 1), ("mfma", 2), ("valu", 2), ("both", 2),
+                               ("split", 2))}
+    out["issue_overlap"] = overlap_summary(times)
+    out["issue_overlap"]["how"] = (f"overlap probe: {cus} blocks (one per CU) of 256 or 512 threads, {ov_iters} "
+                                   "rounds; per round 4 MFMAs and/or the VALU work of 8 probabilities; best of 3")
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     out["hbm_read_gbs"] = round(best(lambda: ha.probe_read(src, sink), 10) / 1e9, 1)
@@ -246,6 +260,24 @@ def achievable_peaks(dev, reps=3):
                   f"best of 3 single launches, and sustained over launches {half + 1}-{2 * half} of {2 * half} "
                   "back to back; 1 GiB read, copy and non-temporal copy, 10 back-to-back launches, best of 3; "
                   "each after a warm-up")
+    return out
+
+
+def overlap_summary(times):
+    """Issue overlap of VALU and MFMA work on one SIMD from the overlap probe's
+    launch times (ms) keyed (mode, waves per SIMD).  valu_hidden: the share of
+    the VALU-only time that a mixed run hides under the MFMAs, (t_m + t_v - t_mixed)
+    / t_v -- 1 with full overlap, 0 when the two run one after the other.  The
+    split run puts one MFMA wave and one VALU wave on each SIMD, so it is read
+    against the one-wave-per-SIMD times."""
+    out = {}
+    for wps in (1, 2):
+        tm, tv, tb = times[("mfma", wps)], times[("valu", wps)], times[("both", wps)]
+        out[f"waves_per_simd_{wps}"] = {"mfma_ms": round(tm, 4), "valu_ms": round(tv, 4), "both_ms": round(tb, 4),
+                                        "valu_hidden": round((tm + tv - tb) / tv, 3)}
+    tm1, tv1, ts = times[("mfma", 1)], times[("valu", 1)], times[("split", 2)]
+    out["split_ms"] = round(ts, 4)
+    out["split_valu_hidden"] = round((tm1 + tv1 - ts) / tv1, 3)
     return out
 
 

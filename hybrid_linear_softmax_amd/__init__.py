@@ -45,6 +45,8 @@ __all__ = [
     "probe_mfma",
     "probe_read",
     "probe_copy",
+    "probe_overlap",
+    "PROBE_OVERLAP_MODES",
     "LAYER_KINDS",
 ]
 
@@ -492,6 +494,25 @@ def probe_mfma(blocks: int, iters: int, sink=None, stream=None) -> float:
     sink = _sink(sink)
     _check(_lib.load().hybrid_attn_probe_mfma(blocks, iters, _ptr(sink), _stream(stream)), "hybrid_attn_probe_mfma")
     return float(_lib.load().hybrid_attn_probe_mfma_flops(blocks, iters))
+
+
+PROBE_OVERLAP_MODES = {"mfma": 0, "valu": 1, "both": 2, "split": 3}
+
+
+@_on_stream
+def probe_overlap(mode: str, waves_per_simd: int, blocks: int, iters: int, sink=None, stream=None) -> dict:
+    """Enqueue the issue-overlap probe (mode "mfma", "valu", "both" or "split");
+    returns the work it performs: bf16 MFMA flops and VALU instructions."""
+    if mode not in PROBE_OVERLAP_MODES:
+        raise ValueError(f"mode must be one of {sorted(PROBE_OVERLAP_MODES)}")
+    sink = _sink(sink)
+    _check(_lib.load().hybrid_attn_probe_overlap(PROBE_OVERLAP_MODES[mode], waves_per_simd, blocks, iters,
+                                                 _ptr(sink), _stream(stream)), "hybrid_attn_probe_overlap")
+    waves = blocks * 4 * waves_per_simd
+    mfma_waves = {"mfma": waves, "valu": 0, "both": waves, "split": waves // 2}[mode]
+    valu_waves = {"mfma": 0, "valu": waves, "both": waves, "split": waves // 2}[mode]
+    return {"mfma_flops": float(mfma_waves) * iters * 4 * 2 * 32 * 32 * 16,
+            "valu_insts": float(valu_waves) * iters * 25}
 
 
 @_on_stream

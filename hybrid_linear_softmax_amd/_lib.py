@@ -54,6 +54,7 @@ SIGNATURES = {
     "hybrid_attn_probe_mfma": (_i, [_i, _i, _p, _p]),
     "hybrid_attn_probe_read": (_i, [_p, _sz, _p, _p]),
     "hybrid_attn_probe_copy": (_i, [_p, _p, _sz, _i, _p]),
+    "hybrid_attn_probe_overlap": (_i, [_i, _i, _i, _i, _p, _p]),
 }
 
 _lib = None

@@ -621,6 +621,16 @@ HA_API int hybrid_attn_probe_mfma(int blocks, int iters, float* sink, hipStream_
   return hip_status(ha::launch_probe_mfma(blocks, iters, sink, stream));
 }
 
+HA_API int hybrid_attn_probe_overlap(int mode, int waves_per_simd, int blocks, int iters, float* sink,
+                                     hipStream_t stream) {
+  if (sink == nullptr || blocks < 1 || blocks > HA_PROBE_MAX_BLOCKS || iters < 1 || iters > HA_PROBE_MAX_ITERS)
+    return HA_EINVAL;
+  if (mode < HA_PROBE_OVERLAP_MFMA || mode > HA_PROBE_OVERLAP_SPLIT) return HA_EINVAL;
+  if (waves_per_simd != 1 && waves_per_simd != 2) return HA_EINVAL;
+  if (mode == HA_PROBE_OVERLAP_SPLIT && waves_per_simd != 2) return HA_EINVAL;
+  return hip_status(ha::launch_probe_overlap(mode, waves_per_simd, blocks, iters, sink, stream));
+}
+
 HA_API int hybrid_attn_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream) {
   if (src == nullptr || sink == nullptr) return HA_EINVAL;
   if (misaligned(src) || bytes % 16 != 0) return HA_EALIGN;

@@ -9,12 +9,18 @@
 //    apply streams with non-temporal ones).  A block covers 4 x 256 consecutive
 //    words per pass (a thread's four words one block-width apart) and the grid
 //    strides over the buffer, so every block streams contiguous memory.
+//  * issue overlap: whether one SIMD runs the anchor's softmax VALU work (fused
+//    multiply-add, exp2, bf16 pack, dot2 row sum) while MFMAs execute, within a
+//    wave and between waves.  One block per CU (its LDS reservation keeps a
+//    second one off), 1 or 2 waves per SIMD; the caller times the MFMA-only,
+//    VALU-only and mixed runs and compares.
 // Each kernel stores to its one-float sink only under a condition that the
 // data practically never meets, which keeps the compiler from dropping the work.
 #include <algorithm>
 
 #include "ha_device.h"
 #include "ha_launch.h"
+#include "../../include/ha_probe.h"
 
 namespace ha {
 
@@ -108,6 +114,103 @@ __global__ __launch_bounds__(kStreamThreads) void probe_copy_kernel(const u32x4*
   }
 }
 
+// Overlap probe.  Per round: the MFMA part is kProbeChains independent 32x32x16
+// bf16 MFMAs on VGPR accumulators (as the anchor's), the VALU part the anchor's
+// instructions for 8 probabilities (8 fused multiply-adds and 8 exp2, 4 bf16
+// pair packs, 4 dot2 row-sum steps) plus one add that moves the maximum they
+// are taken against, so that no round is loop-invariant; BOTH interleaves one
+// MFMA with a quarter of the VALU part (the anchor's logit phase: per MFMA two
+// fused multiply-adds, two exp2, a pack and a dot2).
+constexpr int kOverlapLds = 96 * 1024;  // more than half a CU's LDS: one block per CU
+
+template <int MODE>
+__global__ __launch_bounds__(512) void probe_overlap_kernel(int iters, float* sink) {
+  extern __shared__ int reserve[];
+  const int lane = threadIdx.x & 63;
+  bool do_mfma = MODE == HA_PROBE_OVERLAP_MFMA || MODE == HA_PROBE_OVERLAP_BOTH;
+  bool do_valu = MODE == HA_PROBE_OVERLAP_VALU || MODE == HA_PROBE_OVERLAP_BOTH;
+  if constexpr (MODE == HA_PROBE_OVERLAP_SPLIT) {
+    // roles by placement, not by wave index: the first wave of each SIMD (SIMD
+    // id from the HW_ID register, bits 5:4) takes the VALU part, the rest MFMA
+    if (threadIdx.x < 4) reserve[threadIdx.x] = 0;
+    __syncthreads();
+    const int simd = static_cast<int>((__builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11)) >> 4) & 3);
+    int slot = 0;
+    if (lane == 0) slot = atomicAdd(&reserve[simd], 1);
+    slot = __shfl(slot, 0);
+    do_valu = slot == 0;
+    do_mfma = !do_valu;
+  }
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(static_cast<float>((lane + i) & 7) * 0.0625f);
+    b[i] = static_cast<__bf16>(static_cast<float>((3 * lane + i) & 7) * 0.0625f);
+  }
+  f32x16 acc[kProbeChains];
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  // logit-like inputs, a scale and a running maximum (scaled) as in the
+  // anchor: the maximum grows by 2^-20 a round, so the probabilities stay in
+  // (0, 1] and every sum finite up to the largest iters
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.01f * static_cast<float>(lane + e);
+  const float c = 0.12752977f;
+  float mc = 0.75f;
+  float rowsum = 0.f;
+  const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  auto valu_quarter = [&](int k) {
+    if (k == 0) {
+      mc += 0x1p-20f;
+      asm volatile("" : "+v"(mc));
+    }
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * k], c, -mc));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * k + 1], c, -mc));
+    const uint32_t pk = pack_bf16(p0, p1);
+    rowsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, rowsum, false);
+    asm volatile("" : "+v"(rowsum));
+  };
+  if constexpr (MODE == HA_PROBE_OVERLAP_SPLIT) {
+    if (do_mfma) {
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int k = 0; k < kProbeChains; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+    } else {
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) valu_quarter(k);
+    }
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (do_mfma) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+        if (do_valu) valu_quarter(k);
+      }
+    }
+  }
+  float r = rowsum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r += x[e];
+#pragma unroll
+  for (int k = 0; k < kProbeChains; ++k)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r += acc[k][q];
+  if (r == -1.0f) sink[0] = r;  // every term is non-negative
+}
+
+template <int MODE>
+hipError_t launch_overlap_mode(int blocks, int threads, int iters, float* sink, hipStream_t s) {
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(probe_overlap_kernel<MODE>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kOverlapLds);
+  if (e != hipSuccess) return e;
+  probe_overlap_kernel<MODE><<<dim3(static_cast<unsigned>(blocks)), dim3(threads), kOverlapLds, s>>>(iters, sink);
+  return hipGetLastError();
+}
+
 unsigned stream_grid(int64_t n) {
   constexpr int64_t span = static_cast<int64_t>(kStreamThreads) * kStreamUnroll;
   return static_cast<unsigned>(std::min(kStreamBlocks, std::max<int64_t>(1, (n + span - 1) / span)));
@@ -123,6 +226,17 @@ double probe_mfma_flops(int blocks, int iters) {
 hipError_t launch_probe_mfma(int blocks, int iters, float* sink, hipStream_t s) {
   probe_mfma_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(iters, sink);
   return hipGetLastError();
+}
+
+hipError_t launch_probe_overlap(int mode, int waves_per_simd, int blocks, int iters, float* sink, hipStream_t s) {
+  const int threads = 256 * waves_per_simd;
+  switch (mode) {
+    case HA_PROBE_OVERLAP_MFMA: return launch_overlap_mode<HA_PROBE_OVERLAP_MFMA>(blocks, threads, iters, sink, s);
+    case HA_PROBE_OVERLAP_VALU: return launch_overlap_mode<HA_PROBE_OVERLAP_VALU>(blocks, threads, iters, sink, s);
+    case HA_PROBE_OVERLAP_BOTH: return launch_overlap_mode<HA_PROBE_OVERLAP_BOTH>(blocks, threads, iters, sink, s);
+    case HA_PROBE_OVERLAP_SPLIT: return launch_overlap_mode<HA_PROBE_OVERLAP_SPLIT>(blocks, threads, iters, sink, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s) {

@@ -292,6 +292,13 @@ def test_probe_errors(lib):
     assert copy(SRC, SRC + 512, 1024, 0, None) == EINVAL       # ranges overlap
     assert copy(SRC, DST + 8, 1024, 1, None) == EALIGN and copy(SRC, DST, 1000, 0, None) == EALIGN
     assert copy(SRC, DST, 0, 0, None) == OK
+    ov = lib.hybrid_attn_probe_overlap
+    assert ov(0, 2, 1, 1, None, None) == EINVAL                # no sink
+    assert ov(-1, 2, 1, 1, SINK, None) == EINVAL and ov(4, 2, 1, 1, SINK, None) == EINVAL   # unknown modes
+    assert ov(0, 0, 1, 1, SINK, None) == EINVAL and ov(0, 3, 1, 1, SINK, None) == EINVAL    # 1 or 2 waves per SIMD
+    assert ov(3, 1, 1, 1, SINK, None) == EINVAL                # the split needs two waves per SIMD
+    assert ov(0, 1, 0, 1, SINK, None) == EINVAL and ov(0, 1, 1, 0, SINK, None) == EINVAL
+    assert ov(0, 1, (1 << 20) + 1, 1, SINK, None) == EINVAL and ov(0, 1, 1, (1 << 24) + 1, SINK, None) == EINVAL
 
 
 def test_noalloc_group_limits(lib):

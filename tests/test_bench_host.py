@@ -178,3 +178,17 @@ def test_single_thread_baselines_on_small_workloads():
     assert "2 of 6 heads" in r["linear_layer_480p"]["sample"]
     # the BLAS thread limit is lifted again afterwards
     assert bench._blas_threads() >= 1
+
+
+def test_overlap_summary_fractions():
+    """valu_hidden is 1 for full overlap (mixed time = the longer part), 0 for
+    none (the sum) and is read per waves-per-SIMD setting; the split run is
+    compared with the one-wave-per-SIMD times."""
+    t = {("mfma", 1): 2.0, ("valu", 1): 1.0, ("both", 1): 2.0,      # full overlap
+         ("mfma", 2): 4.0, ("valu", 2): 2.0, ("both", 2): 6.0,      # none
+         ("split", 2): 2.5}                                         # half of the one-wave VALU time hidden
+    s = bench.overlap_summary(t)
+    assert s["waves_per_simd_1"]["valu_hidden"] == 1.0
+    assert s["waves_per_simd_2"]["valu_hidden"] == 0.0
+    assert s["split_valu_hidden"] == 0.5 and s["split_ms"] == 2.5
+    assert s["waves_per_simd_2"]["mfma_ms"] == 4.0
