@@ -29,6 +29,15 @@ def test_tiny_group_full():
         assert err < TOL["f32"]
 
 
+# Elementwise bounds (max, 99.9th percentile of |got - ref| / |ref| over
+# elements with |ref| >= 1e-2 max |ref|), about three times what the full-size
+# runs measure: the linear layer's elements carry the bf16 rounding of the
+# output (measured max 3.9e-3); the softmax's small elements also carry the
+# bf16 rounding of each probability summed over ~N keys (measured max
+# 0.09-0.16, p99.9 0.03-0.07).  An indexing or masking mistake gives O(1).
+ELEM_BOUND = {"linear": (1.2e-2, 1.2e-2), "softmax": (0.5, 0.2)}
+
+
 @pytest.mark.parametrize("name", [n for n in CONFIGS if n != "tiny"])
 def test_config_group_sampled(name):
     w = get(name)
@@ -45,10 +54,11 @@ def test_config_group_sampled(name):
         heavy = heavy_token_positions(w, l)[:256]
         rows = sample_rows(w.N, n_rand=512 if kind == "softmax" else 4096, seed=l, extra=heavy)
         args = (x["Q"][l], x["K"][l], x["V"][l], x["G"][l], out[l])
-        check_layer_sampled(kind, *args, heads, rows, TOL[w.dtype], f"{name} layer {l}")
+        bound = ELEM_BOUND[kind] if w.dtype == "bf16" else None
+        check_layer_sampled(kind, *args, heads, rows, TOL[w.dtype], f"{name} layer {l}", elem_bound=bound)
         # every other (b, h) on a small seeded sample (a head-indexing or block
         # remap error confined to middle heads would show here)
         check_layer_sampled(kind, *args, others, small_row_sample(w.N, seed=100 + l), TOL[w.dtype],
-                            f"{name} layer {l} (all heads)")
+                            f"{name} layer {l} (all heads)", elem_bound=bound)
     del x, out, ws
     torch.cuda.empty_cache()
