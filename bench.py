@@ -900,7 +900,7 @@ def run_stack(args, w):
         "config": {"workload": f"{w.name}_attnres_stack", "blocks": nb, "B": w.B, "N": w.N, "H": w.H, "d": w.d,
                    "parallelism": "single-gpu"},
         "roofline": {
-            "kernel": f"attnres_mix_kernel ({nb} candidates)",
+            "kernel": f"attnres_mix_bf16_1pass ({nb} candidates, single pass)",
             "bound": "hbm",
             "achieved": round(mix_bytes / (mix_ms / 1e3) / 1e9, 1),
             "peak": HBM_PEAK_GBS,

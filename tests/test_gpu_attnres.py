@@ -28,8 +28,11 @@ def _rand(shape, seed, dtype, scale=1.0):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M", [0, 1, 3])
-@pytest.mark.parametrize("B,N,C", [(1, 1, 128), (2, 300, 192), (1, 777, 3072)])
+@pytest.mark.parametrize("B,N,C", [(1, 1, 128), (2, 300, 192), (1, 777, 3072), (1, 97, 5120), (1, 33, 6400)])
 def test_mix_parity(dtype, M, B, N, C):
+    # bf16 rows of up to 6,144 features take the single-pass kernel (1 to 12
+    # 16-byte chunks per lane: C = 128 and 192 leave lanes idle, 5,120 uses 10),
+    # 6,400 the two-pass one, as does float32
     say(f"attnres mix {dtype} M={M} B={B} N={N} C={C}")
     x = _rand((B, N, C), 1, dtype)
     S = _rand((M, B, N, C), 2, dtype, scale=2.0) if M else None
@@ -43,6 +46,21 @@ def test_mix_parity(dtype, M, B, N, C):
     assert e < TOL[dtype], e
     if M == 0:
         assert torch.equal(h, x)        # one candidate: weight exactly 1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mix_most_candidates(dtype):
+    M, B, N, C = 63, 1, 50, 256           # the largest number of summaries
+    say(f"attnres mix {dtype} M={M} C={C}")
+    x = _rand((B, N, C), 5, dtype)
+    S = _rand((M, B, N, C), 6, dtype, scale=2.0)
+    w = _rand((C,), 7, "f32", scale=4.0)   # peaked weights: the running maximum moves
+    h = ha.hybrid_attn_attnres_mix(S, x, w)
+    torch.cuda.synchronize()
+    ref = oracle.attnres_mix(np.concatenate([to_f64(S), to_f64(x)[None]]), to_f64(w))
+    e = rel_err(to_f64(h), ref)
+    say(f"  max rel err {e:.2e}")
+    assert e < TOL[dtype], e
 
 
 def _routed_inputs(dtype, d, B, N, H, nblocks, out_scale=3.0):
