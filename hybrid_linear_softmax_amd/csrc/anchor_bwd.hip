@@ -353,7 +353,11 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
   // rows 4 m .. 4 m + 3, features 8 fg .. 8 fg + 7
   const int sub = tid & 255;
   const bool loader = sub < TSUB;
-  const bool is_a = tid >= 256;
+  // waves 0-3 fetch Q, waves 4-7 da: the choice is taken from a wave-uniform
+  // value so that the buffer descriptor stays in scalar registers (chosen per
+  // lane, it made the compiler wrap every load in a loop over the distinct
+  // descriptors of the wave)
+  const bool is_a = __builtin_amdgcn_readfirstlane(wave) >= 4;
   const int sfg = sub / (BQ / 4), sm = sub % (BQ / 4);
   const __amdgpu_buffer_rsrc_t rsrc = is_a ? rA : rQ;
   bf16_t* dst_row = is_a ? sA : sQ;
@@ -376,7 +380,10 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
   // row-major writes: in instruction j a thread writes row 4 sm + (j + rot) % 4
   // of its four, so that 8 (or 16) neighbouring lanes, which differ in sm,
   // cover distinct LDS banks; the transposed writes need the rows in order and
-  // go first
+  // go first.  (An XOR swizzle of the rows' 16-byte slots instead of the
+  // rotation would avoid its register moves, but measured with an LDS probe
+  // every swizzle that keeps these writes conflict-free slows the fragment
+  // reads of the tile, which are four times as frequent, by about 30 %.)
   const int rot = ((sm >> 2) + 2 * ((sm >> 1) & 1)) & 3;
   auto commit = [&]() {
     if (loader) {
