@@ -189,7 +189,10 @@ __global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__
   load_tile(0, sK0, sV0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 is in LDS
   __syncthreads();
-  auto step = [&](int64_t kb, const bf16_t* sK, const bf16_t* sV, bf16_t* nK, bf16_t* nV) {
+  // MASKED: the block may hold keys past N (only the last one does); the other
+  // steps skip the per-logit key test
+  auto step = [&](int64_t kb, const bf16_t* sK, const bf16_t* sV, bf16_t* nK, bf16_t* nV, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int64_t k0 = kb * BK;
     if (tid < TSUB) {   // K^T: 4 keys x 8 features per thread
       const int fg = tid / (BK / 4), m = tid % (BK / 4);
@@ -239,7 +242,8 @@ __global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = 32 * t + 8 * (r >> 2) + (r & 3) < limh ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2)) : 0.f;
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
+        const float p = (!MASKED || 32 * t + 8 * (r >> 2) + (r & 3) < limh) ? e : 0.f;
         ds[r] = p * (dp[r] - Dq);
       }
 #pragma unroll
@@ -258,9 +262,19 @@ __global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile is in LDS
     dq_barrier();                        // and everyone is done with this one and K^T
   };
-  for (int64_t kb = 0; kb < nkb; kb += 2) {
-    step(kb, sK0, sV0, sK1, sV1);
-    if (kb + 1 < nkb) step(kb + 1, sK1, sV1, sK0, sV0);
+  using NoMask = std::integral_constant<bool, false>;
+  using Mask = std::integral_constant<bool, true>;
+  // blocks 0 .. nfull - 1 hold 64 valid keys; the last steps (at most two,
+  // including the ragged block) take the masked body
+  const int64_t nfull = N / BK;
+  int64_t kb = 0;
+  for (; kb + 2 <= nfull; kb += 2) {
+    step(kb, sK0, sV0, sK1, sV1, NoMask{});
+    step(kb + 1, sK1, sV1, sK0, sV0, NoMask{});
+  }
+  for (; kb < nkb; kb += 2) {
+    step(kb, sK0, sV0, sK1, sV1, Mask{});
+    if (kb + 1 < nkb) step(kb + 1, sK1, sV1, sK0, sV0, Mask{});
   }
   if (qrow < N) {
     const float scale = c / kLog2e;
