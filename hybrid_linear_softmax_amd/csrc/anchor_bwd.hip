@@ -377,7 +377,16 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
   bf16_t* dst_row = is_a ? sA : sQ;
   bf16_t* dst_t = is_a ? sAt : sQt;
   uint4 pre[4];
+  // lse and D of the next step's queries, as loaded: they are first used at the
+  // commit, so the loads stay in flight during the step's MFMAs (scaling lse
+  // right after its load made the compiler wait there for all of the wave's
+  // loads of the step, the Q/da rows included).  Past N they read as 0.
   float preL = 0.f, preD = 0.f;
+  int64_t preQ = 0;
+  const __amdgpu_buffer_rsrc_t rL =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(lse + bh * N), (short)0, (int)(N * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rD =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Dv + bh * N), (short)0, (int)(N * 4), 0x00020000);
   auto fetch = [&](int64_t q0) {
     if (loader) {
 #pragma unroll
@@ -385,10 +394,9 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
         pre[j] = buffer_load16(rsrc, static_cast<uint32_t>((q0 + 4 * sm + j) * (D * 2) + sfg * 16));
     }
     if (tid < BQ) {
-      const int64_t q = q0 + tid;
-      // a query past N contributes nothing: P = exp2(s c - inf) = 0
-      preL = q < N ? lse[bh * N + q] * kLog2e : INFINITY;
-      preD = q < N ? Dv[bh * N + q] : 0.f;
+      preQ = q0 + tid;
+      preL = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, static_cast<int>(preQ * 4), 0, 0));
+      preD = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, static_cast<int>(preQ * 4), 0, 0));
     }
   };
   // row-major writes: in instruction j a thread writes row 4 sm + (j + rot) % 4
@@ -425,7 +433,8 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
       for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&dst_row[(4 * sm + ((j + rot) & 3)) * KP + 8 * sfg]) = pre[j];
     }
     if (tid < BQ) {
-      sL[tid] = preL;
+      // a query past N contributes nothing: P = exp2(s c - inf) = 0
+      sL[tid] = preQ < N ? preL * kLog2e : INFINITY;
       sD[tid] = preD;
     }
   };
