@@ -34,6 +34,8 @@
 //  * tiles are ordered in groups of 4 token tiles x all feature tiles and the
 //    order is split into 8 contiguous ranges, one per XCD, so the blocks that
 //    run together on one XCD share token rows and weight rows in its L2.
+#include <type_traits>
+
 #include "ha_device.h"
 #include "ha_launch.h"
 
@@ -63,6 +65,13 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 3; }
 // lambda can make the host compilation drop the kernel's launch stub.
 __device__ __forceinline__ void global_to_lds16(const bf16_t* src, bf16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// The same through a buffer descriptor: byte address base + voff (per lane,
+// fixed for the kernel) + soff (wave-uniform, the K step): no vector
+// instruction per load.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, bf16_t* dst, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, static_cast<int>(voff), soff, 0, 0);
 }
 
 // block barrier after this wave's LDS accesses have completed; the sched and
@@ -95,7 +104,9 @@ __device__ __forceinline__ void tile_of(int64_t t, const ProjShape& p, int64_t& 
 // MODE 0: proj_in, X = x [M, K], outputs scattered into out[0..3] = Q, K, V, G.
 // MODE 1: proj_out, X = O [B, H, N, d] read as [M, K], out[0] = resid + X W^T;
 // out0 may be resid itself (each element is read, then written, by one lane).
-template <int MODE>
+// WIDE (proj_out only): O spans 4 GB or more, beyond 32-bit buffer offsets from
+// its start; its token rows are then loaded through 64-bit lane addresses.
+template <int MODE, bool WIDE>
 __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X,
                                                     const bf16_t* __restrict__ W,
                                                     bf16_t* out0, bf16_t* __restrict__ out1,
@@ -105,7 +116,9 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index, and all that derives from it, in scalar registers: load
+  // destinations and descriptors need no per-lane arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
   const int wf = wave >> 2;  // group: 128-feature half, and the half of each stage it loads
@@ -116,25 +129,38 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
   const int nk = static_cast<int>(p.K / kTK);
 
   // Loads: wave (wf, wt) fills rows 64 wt + 16 j .. + 15 (j < 4) of its group's
-  // half of a stage, one 1 KB global_load_lds each; lane L fills row
-  // 64 wt + 16 j + L / 4, slot L % 4, with the row's chunk (L % 4) ^ swz(row).
+  // half of a stage, one 1 KB load each; lane L fills row 64 wt + 16 j + L / 4,
+  // slot L % 4, with the row's chunk (L % 4) ^ swz(row).  The weight rows and
+  // proj_in's token rows are read through a descriptor at the tile's first row
+  // (lane offsets below 256 rows, the K step in the scalar offset); proj_out's
+  // token rows through one at O (lane offset the row in O, scalar offset the
+  // head and feature of the K step), or, for WIDE, through 64-bit addresses.
+  constexpr bool LANE_PTR = MODE == 1 && WIDE;
+  const bool tok_lane_ptr = LANE_PTR && wf == 1;
+  const bf16_t* dbase = wf == 0 ? W + f0 * p.K : (MODE == 0 ? X + m0 * p.K : X);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)dbase, (short)0, -1, 0x00020000);
+  uint32_t voff[4];
   const bf16_t* src[4];
   int ldst[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 64 * wt + 16 * j + (lane >> 2);
     const int chunk = (lane & 3) ^ swz(256 * wf + r);
+    int64_t e;  // element offset of the row's chunk from dbase
     if (wf == 0) {
-      src[j] = W + min(f0 + r, p.Nf - 1) * p.K + 8 * chunk;
+      e = (min(f0 + r, p.Nf - 1) - f0) * p.K;
     } else {
       const int64_t m = min(m0 + r, p.M - 1);
       if (MODE == 0) {
-        src[j] = X + m * p.K + 8 * chunk;
+        e = (m - m0) * p.K;
       } else {
         const int64_t b = m / p.N, n = m - b * p.N;
-        src[j] = X + (b * p.H * p.N + n) * p.d + 8 * chunk;
+        e = (b * p.H * p.N + n) * p.d;
       }
     }
+    e += 8 * chunk;
+    voff[j] = static_cast<uint32_t>(e * 2);
+    if (LANE_PTR) src[j] = dbase + e;
     ldst[j] = (256 * wf + 64 * wt + 16 * j) * kTK;
   }
   // element offset of K step t: weights and proj_in tokens are contiguous in K;
@@ -144,27 +170,36 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
     if (MODE == 0 || wf == 0) return k0;
     return (k0 >> p.lgd) * p.N * p.d + (k0 & (p.d - 1));
   };
-  auto load_stage = [&](int t) {
-    bf16_t* base = lds + (t % kStages) * kStage;
+  // the ring's stage is a template argument (the loops below are unrolled by
+  // the ring's depth), so stage offsets are immediates
+  auto load_stage = [&](auto S, int t) {
+    bf16_t* base = lds + decltype(S)::value * kStage;
     const int64_t off = k_off(t);
+    if (tok_lane_ptr) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) global_to_lds16(src[j] + off, base + ldst[j]);
+      for (int j = 0; j < 4; ++j) global_to_lds16(src[j] + off, base + ldst[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) buffer_to_lds16(rs, base + ldst[j], voff[j], static_cast<int>(off * 2));
+    }
   };
+  // rows 128 wf + 32 fi + l32 and 256 + 64 wt + 32 ti + l32 have the swizzle of l32
+  const int sw = swz(l32);
   bf16x8 a[4][2], bx[2][2];
-  auto read_operands = [&](int t) {
-    const bf16_t* base = lds + (t % kStages) * kStage;
+  auto read_operands = [&](auto S) {
+    const bf16_t* base = lds + decltype(S)::value * kStage;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int c = 2 * kk + h;
+      const int c = (2 * kk + h) ^ sw;
 #pragma unroll
       for (int fi = 0; fi < 4; ++fi) {
         const int row = 128 * wf + 32 * fi + l32;
-        a[fi][kk] = *reinterpret_cast<const bf16x8*>(base + row * kTK + 8 * (c ^ swz(row)));
+        a[fi][kk] = *reinterpret_cast<const bf16x8*>(base + row * kTK + 8 * c);
       }
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
         const int row = 256 + 64 * wt + 32 * ti + l32;
-        bx[ti][kk] = *reinterpret_cast<const bf16x8*>(base + row * kTK + 8 * (c ^ swz(row)));
+        bx[ti][kk] = *reinterpret_cast<const bf16x8*>(base + row * kTK + 8 * c);
       }
     }
   };
@@ -189,8 +224,15 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
   // by group 0 in the second phase of pair t - 1, by group 1 in the first phase
   // of pair t.  Before the barrier that precedes group 0's read, every wave waits
   // until at most its loads of later steps are outstanding (4 per step).
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  static_assert(kStages == 4, "the loops are unrolled by the ring's depth");
   const int pre = min(nk, 3);
-  for (int t = 0; t < pre; ++t) load_stage(t);
+  load_stage(S0{}, 0);
+  if (pre > 1) load_stage(S1{}, 1);
+  if (pre > 2) load_stage(S2{}, 2);
   if (pre == 3) {
     HA_WAIT_VMCNT(8);
   } else if (pre == 2) {
@@ -199,32 +241,47 @@ __global__ __launch_bounds__(512, 1) void proj_bf16(const bf16_t* __restrict__ X
     HA_WAIT_VMCNT(0);
   }
   phase_barrier();
+  // step s of a group; U = s mod 4 (the stage step s occupies)
+  auto step0 = [&](auto U, int s) {
+    constexpr int u = decltype(U)::value;
+    compute();
+    if (s + 2 < nk) {
+      HA_WAIT_VMCNT(4);  // step s + 2 may stay in flight
+    } else {
+      HA_WAIT_VMCNT(0);
+    }
+    phase_barrier();
+    if (s + 1 < nk) read_operands(std::integral_constant<int, (u + 1) % 4>{});
+    if (s + 3 < nk) load_stage(std::integral_constant<int, (u + 3) % 4>{}, s + 3);
+    phase_barrier();
+  };
+  auto step1 = [&](auto U, int s) {
+    constexpr int u = decltype(U)::value;
+    read_operands(U);
+    if (s + 3 < nk) {
+      load_stage(std::integral_constant<int, (u + 3) % 4>{}, s + 3);
+      HA_WAIT_VMCNT(8);  // steps s + 2 and s + 3 may stay in flight
+    } else {
+      HA_WAIT_VMCNT(0);
+    }
+    phase_barrier();
+    compute();
+    phase_barrier();
+  };
   if (wf == 0) {
-    read_operands(0);
-    for (int s = 0; s < nk; ++s) {
-      compute();
-      if (s + 2 < nk) {
-        HA_WAIT_VMCNT(4);  // step s + 2 may stay in flight
-      } else {
-        HA_WAIT_VMCNT(0);
-      }
-      phase_barrier();
-      if (s + 1 < nk) read_operands(s + 1);
-      if (s + 3 < nk) load_stage(s + 3);
-      phase_barrier();
+    read_operands(S0{});
+    for (int s = 0; s < nk; s += 4) {
+      step0(S0{}, s);
+      if (s + 1 < nk) step0(S1{}, s + 1);
+      if (s + 2 < nk) step0(S2{}, s + 2);
+      if (s + 3 < nk) step0(S3{}, s + 3);
     }
   } else {
-    for (int s = 0; s < nk; ++s) {
-      read_operands(s);
-      if (s + 3 < nk) {
-        load_stage(s + 3);
-        HA_WAIT_VMCNT(8);  // steps s + 2 and s + 3 may stay in flight
-      } else {
-        HA_WAIT_VMCNT(0);
-      }
-      phase_barrier();
-      compute();
-      phase_barrier();
+    for (int s = 0; s < nk; s += 4) {
+      step1(S0{}, s);
+      if (s + 1 < nk) step1(S1{}, s + 1);
+      if (s + 2 < nk) step1(S2{}, s + 2);
+      if (s + 3 < nk) step1(S3{}, s + 3);
     }
   }
 
@@ -355,10 +412,20 @@ hipError_t launch_proj(bool bf16, const void* X, const void* W, void* o0, void* 
   const ProjShape p = shape(B, H, N, d, MODE == 0);
   if (p.M == 0 || p.K == 0) return hipSuccess;
   if (bf16) {
-    proj_bf16<MODE><<<dim3(static_cast<unsigned>(p.total)), dim3(512), 0, s>>>(
-        static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(o0),
-        static_cast<bf16_t*>(o1), static_cast<bf16_t*>(o2), static_cast<bf16_t*>(o3),
-        static_cast<const bf16_t*>(resid), p);
+    auto go = [&](auto kern) {
+      kern<<<dim3(static_cast<unsigned>(p.total)), dim3(512), 0, s>>>(
+          static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(o0),
+          static_cast<bf16_t*>(o1), static_cast<bf16_t*>(o2), static_cast<bf16_t*>(o3),
+          static_cast<const bf16_t*>(resid), p);
+    };
+    // proj_out's buffer offsets into O are 32-bit byte offsets from its start
+    if constexpr (MODE == 1) {
+      if (p.M * p.K * 2 >= (int64_t{1} << 32)) {
+        go(proj_bf16<MODE, true>);
+        return hipGetLastError();
+      }
+    }
+    go(proj_bf16<MODE, false>);
   } else {
     const int64_t blocks = ((p.M + 63) / 64) * ((p.Nf + 63) / 64);
     proj_f32<MODE><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(

@@ -183,3 +183,26 @@ def test_14b_b2_projections_sampled():
     assert e < TOL["bf16"]
     del t, Q, O, x1
     torch.cuda.empty_cache()
+
+
+def test_proj_out_wide_sampled():
+    # O of exactly 4 GiB (B = 1, N = 2^20, C = 2048): its byte offsets no longer
+    # fit 32 bits, so proj_out loads its token rows through 64-bit lane
+    # addresses; rows sampled across the tensor, the last one included
+    B, N, H, d = 1, 1 << 20, 16, 128
+    C = H * d
+    say(f"proj_out with a 4 GiB O: B={B} N={N} C={C}")
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    O = torch.randn((B, H, N, d), generator=gen, device=DEV, dtype=torch.bfloat16) * 0.05
+    assert O.numel() * O.element_size() == 1 << 32
+    x = torch.randn((B, N, C), generator=gen, device=DEV, dtype=torch.bfloat16)
+    W = (torch.randn((C, C), generator=gen, device=DEV, dtype=torch.float32) / C ** 0.5).to(torch.bfloat16)
+    x1 = ha.hybrid_attn_proj_out(O, W, x)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, n_rand=48, seed=12)
+    ref = oracle.project_out(to_f64(O[:, :, rows]), to_f64(W), to_f64(x[:, rows]))
+    e = rel_err(to_f64(x1[:, rows]), ref)
+    say(f"  sampled rows: {e:.2e}")
+    assert e < TOL["bf16"]
+    del O, x, W, x1
+    torch.cuda.empty_cache()
