@@ -20,13 +20,17 @@
 //    next K step and the loads of a K step three ahead -- so that in every phase
 //    one wave per SIMD keeps the matrix core busy.  Each group runs a loop of its
 //    own (phases in opposite order), with no role branch inside it;
-//  * K tiles come straight from global memory into LDS (global_load_lds, 16
+//  * K tiles come straight from global memory into LDS (buffer loads to LDS, 16
 //    bytes per lane, no registers): a ring of four 32 KB stages, rows of 64 bytes
 //    whose 16-byte chunks are XOR-swizzled by row so that the fragment reads of
 //    32 consecutive rows hit distinct banks; group 0 loads the weight half of a
-//    stage, group 1 the token half.  Waits on those loads are explicit (the
-//    compiler does not track them), placed before the barrier that precedes a
-//    stage's first read;
+//    stage, group 1 the token half.  A lane's offset is fixed for the kernel and
+//    the K step is the scalar offset, the wave index sits in a scalar register
+//    and the loops are unrolled by the ring's depth, so neither the loads nor the
+//    fragment reads need per-lane address arithmetic (on this part vector
+//    instructions of one wave do not issue under another wave's MFMAs).  Waits
+//    on those loads are explicit (the compiler does not track them), placed
+//    before the barrier that precedes a stage's first read;
 //  * proj_out reads its token rows straight out of O's [B, H, N, d] layout: a
 //    32-wide K step lies inside one head, so a row is 64 contiguous bytes;
 //  * tiles past M tokens or the last feature clamp their load rows to the last
