@@ -372,41 +372,58 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
   // lane, it made the compiler wrap every load in a loop over the distinct
   // descriptors of the wave)
   const bool is_a = __builtin_amdgcn_readfirstlane(wave) >= 4;
-  const int sfg = sub / (BQ / 4), sm = sub % (BQ / 4);
+  // this thread's sub-tile: 4 query rows 4 sm .. 4 sm + 3, features 8 sfg ..
+  // 8 sfg + 7.  Lane l of the tensor's wave w' takes sm = (l & 7) | (l & 16) >> 1
+  // and sfg = 4 w' + (l >> 3 & 1) + (l >> 5 & 1) * 2: any 16 neighbouring lanes
+  // hold 8 sm x 2 sfg, any 32 hold 16 sm x 2 sfg.  The transposed 8-byte writes
+  // (32 lanes at a time) then cover 32 distinct bank pairs; the row-major
+  // 16-byte writes (16 lanes at a time) do too once the threads with sm bit 2
+  // set hold their rows rotated by two, 4 sm + 2, + 3, + 0, + 1, which they
+  // load in that order (so no register moves: a per-lane rotation of the
+  // registers cost 26 vector instructions per step).  Their transposed words
+  // then carry the query pairs swapped; those are the queries with bit 4 set,
+  // the second 16-query half of each 32, and the P and dS operands of that
+  // half are packed with their pairs swapped to match.  (An XOR swizzle of the
+  // rows' 16-byte slots instead measured, with an LDS probe, ~30 % slower for
+  // the tile's fragment reads, four times as frequent as its writes.)
+  const int ll = sub & 63;
+  const int sfg = 4 * (sub >> 6) + ((ll >> 3) & 1) + 2 * ((ll >> 5) & 1);
+  const int sm = (ll & 7) | ((ll & 16) >> 1);
+  const int rot = 2 * ((sm >> 2) & 1);
   const __amdgpu_buffer_rsrc_t rsrc = is_a ? rA : rQ;
   bf16_t* dst_row = is_a ? sA : sQ;
   bf16_t* dst_t = is_a ? sAt : sQt;
+  // rows 4 sm + rot, + 1 and 4 sm + (rot ^ 2), + 1: two lane offsets, the step
+  // in the scalar offset
+  const int offA = (4 * sm + rot) * (D * 2) + sfg * 16;
+  const int offB = (4 * sm + (rot ^ 2)) * (D * 2) + sfg * 16;
+  bf16_t* rowA = dst_row + (4 * sm + rot) * KP + 8 * sfg;
+  bf16_t* rowB = dst_row + (4 * sm + (rot ^ 2)) * KP + 8 * sfg;
   uint4 pre[4];
   // lse and D of the next step's queries, as loaded: they are first used at the
   // commit, so the loads stay in flight during the step's MFMAs (scaling lse
   // right after its load made the compiler wait there for all of the wave's
   // loads of the step, the Q/da rows included).  Past N they read as 0.
   float preL = 0.f, preD = 0.f;
-  int64_t preQ = 0;
+  int preQ = 0;
   const __amdgpu_buffer_rsrc_t rL =
       __builtin_amdgcn_make_buffer_rsrc((void*)(lse + bh * N), (short)0, (int)(N * 4), 0x00020000);
   const __amdgpu_buffer_rsrc_t rD =
       __builtin_amdgcn_make_buffer_rsrc((void*)(Dv + bh * N), (short)0, (int)(N * 4), 0x00020000);
   auto fetch = [&](int64_t q0) {
     if (loader) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pre[j] = buffer_load16(rsrc, static_cast<uint32_t>((q0 + 4 * sm + j) * (D * 2) + sfg * 16));
+      const int soff = static_cast<int>(q0 * (D * 2));
+      pre[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offA, soff, 0));
+      pre[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offA + D * 2, soff, 0));
+      pre[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offB, soff, 0));
+      pre[3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offB + D * 2, soff, 0));
     }
     if (tid < BQ) {
-      preQ = q0 + tid;
-      preL = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, static_cast<int>(preQ * 4), 0, 0));
-      preD = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, static_cast<int>(preQ * 4), 0, 0));
+      preQ = static_cast<int>(q0) + tid;
+      preL = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, preQ * 4, 0, 0));
+      preD = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, preQ * 4, 0, 0));
     }
   };
-  // row-major writes: in instruction j a thread writes row 4 sm + (j + rot) % 4
-  // of its four, so that 8 (or 16) neighbouring lanes, which differ in sm,
-  // cover distinct LDS banks; the transposed writes need the rows in order and
-  // go first.  (An XOR swizzle of the rows' 16-byte slots instead of the
-  // rotation would avoid its register moves, but measured with an LDS probe
-  // every swizzle that keeps these writes conflict-free slows the fragment
-  // reads of the tile, which are four times as frequent, by about 30 %.)
-  const int rot = ((sm >> 2) + 2 * ((sm >> 1) & 1)) & 3;
   auto commit = [&]() {
     if (loader) {
       const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&pre[0]);
@@ -421,16 +438,10 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
         *reinterpret_cast<uint2*>(&dst_t[(8 * sfg + 2 * p + 1) * TP + pos]) =
             make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u), __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
       }
-      if (rot & 1) {
-        const uint4 t0 = pre[0];
-        pre[0] = pre[1]; pre[1] = pre[2]; pre[2] = pre[3]; pre[3] = t0;
-      }
-      if (rot & 2) {
-        const uint4 t0 = pre[0], t1 = pre[1];
-        pre[0] = pre[2]; pre[1] = pre[3]; pre[2] = t0; pre[3] = t1;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&dst_row[(4 * sm + ((j + rot) & 3)) * KP + 8 * sfg]) = pre[j];
+      *reinterpret_cast<uint4*>(rowA) = pre[0];
+      *reinterpret_cast<uint4*>(rowA + KP) = pre[1];
+      *reinterpret_cast<uint4*>(rowB) = pre[2];
+      *reinterpret_cast<uint4*>(rowB + KP) = pre[3];
     }
     if (tid < BQ) {
       // a query past N contributes nothing: P = exp2(s c - inf) = 0
@@ -490,6 +501,10 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
       pk.z = pack_bf16(p[8 * tt + 4], p[8 * tt + 5]); pk.w = pack_bf16(p[8 * tt + 6], p[8 * tt + 7]);
       dk4.x = pack_bf16(ds[8 * tt + 0], ds[8 * tt + 1]); dk4.y = pack_bf16(ds[8 * tt + 2], ds[8 * tt + 3]);
       dk4.z = pack_bf16(ds[8 * tt + 4], ds[8 * tt + 5]); dk4.w = pack_bf16(ds[8 * tt + 6], ds[8 * tt + 7]);
+      if (tt == 1) {   // the transposed tiles hold these queries' pairs swapped
+        pk = make_uint4(pk.y, pk.x, pk.w, pk.z);
+        dk4 = make_uint4(dk4.y, dk4.x, dk4.w, dk4.z);
+      }
       const bf16x8 pf = as_bf16x8(pk), dsf = as_bf16x8(dk4);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
