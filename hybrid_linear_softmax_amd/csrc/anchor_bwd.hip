@@ -223,8 +223,9 @@ __global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16 s, dp;
+      // dP accumulates onto -D of the lane's query: the MFMAs return dP - D
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = -Dq; }
       bf16x8 fk[2], fv[2];
       auto frag = [&](int st, int b) {
         const int off = (32 * t + l32) * D + 8 * ((2 * st + h) ^ sw);
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__
       for (int r = 0; r < 16; ++r) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
         const float p = (!MASKED || 32 * t + 8 * (r >> 2) + (r & 3) < limh) ? e : 0.f;
-        ds[r] = p * (dp[r] - Dq);
+        ds[r] = p * dp[r];
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
     if (tid < BQ) {
       // a query past N contributes nothing: P = exp2(s c - inf) = 0
       sL[tid] = preQ < N ? preL * kLog2e : INFINITY;
-      sD[tid] = preD;
+      sD[tid] = -preD;
     }
   };
 
@@ -460,7 +461,14 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
     const int t = th;
     f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    // dP accumulates onto -D of its rows (sD holds -D), so the MFMAs return
+    // dP - D and dS needs one multiply per element
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 D4 = *reinterpret_cast<const float4*>(&sD[32 * t + 8 * g + 4 * h]);
+      dp[4 * g + 0] = D4.x; dp[4 * g + 1] = D4.y; dp[4 * g + 2] = D4.z; dp[4 * g + 3] = D4.w;
+    }
     // S and dP with each k-slice's fragments read one slice ahead
     bf16x8 fq[2], fa[2], fk[2], fv[2];
     auto frag = [&](int st, int b) {
@@ -480,14 +488,12 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
     float p[16], ds[16];
     auto probs = [&](int g) {  // P and dS of accumulator rows 4 g .. 4 g + 3
       const float4 L4 = *reinterpret_cast<const float4*>(&sL[32 * t + 8 * g + 4 * h]);
-      const float4 D4 = *reinterpret_cast<const float4*>(&sD[32 * t + 8 * g + 4 * h]);
       const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
-      const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g + j;
         p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -Lr[j]));
-        ds[r] = p[r] * (dp[r] - Dr[j]);
+        ds[r] = p[r] * dp[r];
       }
     };
     // the second half's P and dS are computed in the shadow of the first
