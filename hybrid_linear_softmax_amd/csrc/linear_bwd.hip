@@ -35,8 +35,10 @@ __device__ __forceinline__ float pos(float x) { return x > 0.f ? 1.f : 0.f; }
 //   kEpiDQ: vec = z, E1 = Q, rowv = dden -> out1 = (acc + dden z) [Q > 0]
 //   kEpiDV:                   -> out1 = acc
 //   kEpiDK: vec = dz, E1 = K  -> out1 = (acc + dz) [K > 0]
+// Two blocks per CU at least: the compiler keeps every epilogue within 256
+// registers (the n-pass epilogue took 268, which left one block per CU).
 template <int D, int EPI>
-__global__ __launch_bounds__(256) void tgemm_bf16(const bf16_t* __restrict__ X,
+__global__ __launch_bounds__(256, 2) void tgemm_bf16(const bf16_t* __restrict__ X,
                                                   const bf16_t* __restrict__ Mt_hi,
                                                   const bf16_t* __restrict__ Mt_lo,
                                                   const float* __restrict__ vec,
