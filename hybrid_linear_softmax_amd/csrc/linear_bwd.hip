@@ -87,24 +87,25 @@ __global__ __launch_bounds__(256, 2) void tgemm_bf16(const bf16_t* __restrict__ 
 #pragma unroll
   for (int k = 0; k < 8; ++k) vf[k] = HAS_VEC ? vec[bh * D + 8 * fg + k] : 0.f;
 
+  // block blk of a head takes its tiles blk, blk + B, blk + 2B, ... (B blocks
+  // per head): the blocks in flight sweep the head's rows as one front
   const int64_t ntiles = (N + kTok - 1) / kTok;
-  const int64_t tb = blk * tiles_per_block;
-  const int64_t te = min(ntiles, tb + tiles_per_block);
+  const int64_t tstride = blocks_per_head;
 
   uint4 xv[CH], e1v[CH], e2v[CH];
   auto load_tile = [&](int64_t t) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int64_t tok = t * kTok + (tid + 256 * i) / FG;
-      const bool ok = t < te && tok < N;
+      const bool ok = t < ntiles && tok < N;
       const int64_t off = base + tok * D + 8 * fg;
       xv[i] = ok ? *reinterpret_cast<const uint4*>(X + off) : make_uint4(0, 0, 0, 0);
       e1v[i] = (HAS_E1 && ok) ? *reinterpret_cast<const uint4*>(E1 + off) : make_uint4(0, 0, 0, 0);
       e2v[i] = (HAS_E2 && ok) ? *reinterpret_cast<const uint4*>(E2 + off) : make_uint4(0, 0, 0, 0);
     }
   };
-  load_tile(tb);
-  for (int64_t t = tb; t < te; ++t) {
+  load_tile(blk);
+  for (int64_t t = blk; t < ntiles; t += tstride) {
     const int64_t tok0 = t * kTok;
     uint4 e1c[CH], e2c[CH];
 #pragma unroll
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void tgemm_bf16(const bf16_t* __restrict__ 
       *reinterpret_cast<uint4*>(sX + row * XP + 8 * fg) = x;
     }
     __syncthreads();
-    load_tile(t + 1);
+    load_tile(t + tstride);
 #pragma unroll
     for (int mb = 0; mb < kTok / 16; ++mb) {
       f32x4 acc[NB];
