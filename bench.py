@@ -33,7 +33,9 @@ residual); one extra untimed-for-value pass times each stage on its own.
 Every line also carries `achievable` -- what this part sustains, measured after
 the timed steps with the library's probe kernels (an MFMA loop and HBM read and
 copy streams, include/ha_probe.h) -- with the roofline's rate against it as
-`roofline.frac_of_achievable`, and `telemetry`: the GPU clock and socket power
+`roofline.frac_of_achievable` (for an MFMA-bound kernel also against the MFMA
+loop on random operands, `roofline.frac_of_achievable_random_operands`), and
+`telemetry`: the GPU clock and socket power
 sampled through amdsmi while the step repeats, untimed, for about 2.5 s after
 the timed steps (the device refreshes those metrics about once a second; null
 where that interface is unavailable).
@@ -199,7 +201,10 @@ def achievable_peaks(dev, reps=3):
     so that launch gaps do not count) after one warm-up each.  The MFMA loop is
     also run back to back for about 2 s and timed over the second half, once the
     power management has settled (`mfma_bf16_tflops_sustained`, with the clock
-    and power of that half)."""
+    and power of that half), and so is the loop on operands that change every
+    instruction (`mfma_bf16_tflops_random_operands_sustained`): constant
+    operands leave the matrix cores' inputs still, which keeps their power, and
+    so the power limit's hold on the clock, below what real data costs."""
     import torch
 
     import hybrid_linear_softmax_amd as ha
@@ -236,6 +241,22 @@ def achievable_peaks(dev, reps=3):
         torch.cuda.synchronize()
     out["mfma_bf16_tflops_sustained"] = round(flops / (ev[1].elapsed_time(ev[2]) / 1e3) / 1e12, 1)
     out["mfma_sustained_telemetry"] = tele.summary()
+    # the same on operands that change every instruction (random bf16): the
+    # matrix cores' power, and with it the clock the power limit allows, depends
+    # on their inputs toggling
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    flops = sum(ha.probe_mfma_data(blocks, iters, sink) for _ in range(half))
+    ev[1].record()
+    torch.cuda.synchronize()
+    tele = Telemetry(dev.index)
+    with tele:
+        for _ in range(half):
+            ha.probe_mfma_data(blocks, iters, sink)
+        ev[2].record()
+        torch.cuda.synchronize()
+    out["mfma_bf16_tflops_random_operands_sustained"] = round(flops / (ev[1].elapsed_time(ev[2]) / 1e3) / 1e12, 1)
+    out["mfma_random_operands_telemetry"] = tele.summary()
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     ov_iters = 20000
     def launch_ms(mode, wps):
@@ -296,6 +317,10 @@ def annotate(line, peaks, telemetry):
         if ach:
             r["achievable_peak"] = ach
             r["frac_of_achievable"] = round(r["achieved"] / ach, 4)
+        rnd = peaks.get("mfma_bf16_tflops_random_operands_sustained") if r.get("bound") == "mfma" else None
+        if rnd:
+            r["achievable_peak_random_operands"] = rnd
+            r["frac_of_achievable_random_operands"] = round(r["achieved"] / rnd, 4)
     return line
 
 

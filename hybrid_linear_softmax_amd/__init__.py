@@ -43,6 +43,7 @@ __all__ = [
     "hybrid_attn_block",
     "block_workspace_bytes",
     "probe_mfma",
+    "probe_mfma_data",
     "probe_read",
     "probe_copy",
     "probe_overlap",
@@ -493,6 +494,16 @@ def probe_mfma(blocks: int, iters: int, sink=None, stream=None) -> float:
     """Enqueue the MFMA throughput probe; returns the flop count it performs."""
     sink = _sink(sink)
     _check(_lib.load().hybrid_attn_probe_mfma(blocks, iters, _ptr(sink), _stream(stream)), "hybrid_attn_probe_mfma")
+    return float(_lib.load().hybrid_attn_probe_mfma_flops(blocks, iters))
+
+
+@_on_stream
+def probe_mfma_data(blocks: int, iters: int, sink=None, stream=None) -> float:
+    """Enqueue the MFMA probe on operands that change every instruction (random
+    bf16); returns the flop count it performs."""
+    sink = _sink(sink)
+    _check(_lib.load().hybrid_attn_probe_mfma_data(blocks, iters, _ptr(sink), _stream(stream)),
+           "hybrid_attn_probe_mfma_data")
     return float(_lib.load().hybrid_attn_probe_mfma_flops(blocks, iters))
 
 

@@ -52,6 +52,7 @@ SIGNATURES = {
     "hybrid_attn_block": (_i, [_p, _p, _p, _p, _i, _i, _i64, _i, _i, _p, _sz, _p]),
     "hybrid_attn_probe_mfma_flops": (ctypes.c_double, [_i, _i]),
     "hybrid_attn_probe_mfma": (_i, [_i, _i, _p, _p]),
+    "hybrid_attn_probe_mfma_data": (_i, [_i, _i, _p, _p]),
     "hybrid_attn_probe_read": (_i, [_p, _sz, _p, _p]),
     "hybrid_attn_probe_copy": (_i, [_p, _p, _sz, _i, _p]),
     "hybrid_attn_probe_overlap": (_i, [_i, _i, _i, _i, _p, _p]),

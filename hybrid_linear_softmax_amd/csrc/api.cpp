@@ -621,6 +621,12 @@ HA_API int hybrid_attn_probe_mfma(int blocks, int iters, float* sink, hipStream_
   return hip_status(ha::launch_probe_mfma(blocks, iters, sink, stream));
 }
 
+HA_API int hybrid_attn_probe_mfma_data(int blocks, int iters, float* sink, hipStream_t stream) {
+  if (sink == nullptr || blocks < 1 || blocks > HA_PROBE_MAX_BLOCKS || iters < 1 || iters > HA_PROBE_MAX_ITERS)
+    return HA_EINVAL;
+  return hip_status(ha::launch_probe_mfma_data(blocks, iters, sink, stream));
+}
+
 HA_API int hybrid_attn_probe_overlap(int mode, int waves_per_simd, int blocks, int iters, float* sink,
                                      hipStream_t stream) {
   if (sink == nullptr || blocks < 1 || blocks > HA_PROBE_MAX_BLOCKS || iters < 1 || iters > HA_PROBE_MAX_ITERS)

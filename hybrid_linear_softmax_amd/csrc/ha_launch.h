@@ -90,6 +90,7 @@ hipError_t launch_proj_out(bool bf16, const void* O, const void* W_out, const vo
 // Achievable-peak probes (see probe.hip).
 double probe_mfma_flops(int blocks, int iters);
 hipError_t launch_probe_mfma(int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_probe_mfma_data(int blocks, int iters, float* sink, hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, bool nontemporal, hipStream_t s);
 hipError_t launch_probe_overlap(int mode, int waves_per_simd, int blocks, int iters, float* sink, hipStream_t s);

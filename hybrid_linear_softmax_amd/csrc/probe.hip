@@ -3,7 +3,8 @@
 // reach them, so that a kernel's rate can be read against both the published
 // peak and what the chip delivers under its own clocks and power limit.
 //  * MFMA: chains of independent v_mfma_f32_32x32x16_bf16 (the instruction of
-//    the anchor and the projections) on register operands, no memory traffic;
+//    the anchor and the projections) on register operands, no memory traffic,
+//    on constant operands and on operands that change with every instruction;
 //  * HBM: a read of 16-byte words (XOR-folded) and a copy, four 16-byte accesses
 //    in flight per thread, the copy with ordinary or non-temporal accesses (the
 //    apply streams with non-temporal ones).  A block covers 4 x 256 consecutive
@@ -55,6 +56,59 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* sink)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[c][r];
   if (s == -1.0f) sink[0] = s;  // the sums are non-negative
+}
+
+// The same chains on operands that change with every instruction: each lane
+// holds 8 operand pairs of pseudo-random bf16 (random sign and mantissa,
+// magnitudes 0.5 to 4, the range of the attention inputs' larger values) and
+// cycles through them, so the multipliers' inputs toggle as they do on real
+// data.  A matrix core's power depends on that toggling: on constant operands
+// the part holds its top clock under the power limit, on data like this it
+// may not.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_data_kernel(int iters, float* sink) {
+  constexpr int kSets = 8;
+  const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 0x9e3779b9u;
+  bf16x8 a[kSets], b[kSets];
+#pragma unroll
+  for (int k = 0; k < kSets; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ha = probe_hash(seed + 16u * k + i);
+      const uint32_t hb = probe_hash(seed + 16u * k + 8 + i);
+      // sign bit, exponent 126..128 (0.5 <= |x| < 4), 7 mantissa bits
+      a[k][i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>((ha & 0x807fu) | ((126u + (ha >> 16) % 3u) << 7)));
+      b[k][i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>((hb & 0x807fu) | ((126u + (hb >> 16) % 3u) << 7)));
+    }
+  f32x16 acc[kProbeChains];
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  static_assert(kSets == 2 * kProbeChains, "two rounds of the chains per pass over the sets");
+  for (int it = 0; it + 2 <= iters; it += 2) {
+#pragma unroll
+    for (int k = 0; k < kSets; ++k)
+      acc[k % kProbeChains] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[k], acc[k % kProbeChains], 0, 0, 0);
+  }
+  if (iters & 1) {
+#pragma unroll
+    for (int c = 0; c < kProbeChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if (s != s) sink[0] = s;  // finite operands: the sum is never NaN
 }
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
@@ -225,6 +279,11 @@ double probe_mfma_flops(int blocks, int iters) {
 
 hipError_t launch_probe_mfma(int blocks, int iters, float* sink, hipStream_t s) {
   probe_mfma_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_data(int blocks, int iters, float* sink, hipStream_t s) {
+  probe_mfma_data_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(iters, sink);
   return hipGetLastError();
 }
 

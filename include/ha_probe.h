@@ -38,6 +38,15 @@ HA_API double hybrid_attn_probe_mfma_flops(int blocks, int iters);
  * HA_EINVAL: sink null, blocks or iters outside their limits. */
 HA_API int hybrid_attn_probe_mfma(int blocks, int iters, float* sink, hipStream_t stream);
 
+/* The same MFMA chains (same grid, the same work: hybrid_attn_probe_mfma_flops)
+ * on operands that change with every instruction: each lane cycles through 8
+ * operand pairs of pseudo-random bf16 (random sign and mantissa, magnitudes in
+ * [0.5, 4)), so the matrix cores' inputs toggle as on real data.  Their power
+ * draw depends on that toggling: the rate this sustains under the part's power
+ * limit is what a kernel streaming real data through the MFMAs can approach.
+ * sink as for hybrid_attn_probe_mfma.  HA_EINVAL: as hybrid_attn_probe_mfma. */
+HA_API int hybrid_attn_probe_mfma_data(int blocks, int iters, float* sink, hipStream_t stream);
+
 /* Issue overlap of one SIMD: does the softmax's VALU work of the anchor run
  * while MFMAs execute, within one wave and between the waves of a SIMD?
  * `blocks` blocks (the CU count fills the part once) of 256 * waves_per_simd

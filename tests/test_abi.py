@@ -283,6 +283,9 @@ def test_probe_errors(lib):
     mfma = lib.hybrid_attn_probe_mfma
     assert mfma(0, 1, SINK, None) == EINVAL and mfma(1, 0, SINK, None) == EINVAL
     assert mfma((1 << 20) + 1, 1, SINK, None) == EINVAL and mfma(1, 1, None, None) == EINVAL
+    data = lib.hybrid_attn_probe_mfma_data
+    assert data(0, 1, SINK, None) == EINVAL and data(1, 0, SINK, None) == EINVAL
+    assert data(1, (1 << 24) + 1, SINK, None) == EINVAL and data(1, 1, None, None) == EINVAL
     read = lib.hybrid_attn_probe_read
     assert read(None, 1024, SINK, None) == EINVAL and read(SRC, 1024, None, None) == EINVAL
     assert read(SRC + 8, 1024, SINK, None) == EALIGN and read(SRC, 1000, SINK, None) == EALIGN

@@ -116,6 +116,17 @@ def test_annotate_adds_fraction_of_achievable():
     line = {"roofline": {"bound": "mfma", "achieved": 1000.0}}
     bench.annotate(line, dict(peaks, mfma_bf16_tflops_sustained=1600.0), None)
     assert line["roofline"]["achievable_peak"] == 1600.0 and line["roofline"]["frac_of_achievable"] == 0.625
+    # the MFMA loop on random operands, where measured, is reported beside it;
+    # an HBM-bound line does not take it
+    both = dict(peaks, mfma_bf16_tflops_sustained=1600.0, mfma_bf16_tflops_random_operands_sustained=1250.0)
+    line = {"roofline": {"bound": "mfma", "achieved": 1000.0}}
+    bench.annotate(line, both, None)
+    assert line["roofline"]["achievable_peak"] == 1600.0
+    assert line["roofline"]["achievable_peak_random_operands"] == 1250.0
+    assert line["roofline"]["frac_of_achievable_random_operands"] == 0.8
+    line = {"roofline": {"bound": "hbm", "achieved": 3200.0}}
+    bench.annotate(line, both, None)
+    assert "achievable_peak_random_operands" not in line["roofline"]
     line = {"roofline": {"bound": "mfma", "achieved": 1.0}}
     bench.annotate(line, None, None)                 # --no-peaks
     assert "achievable_peak" not in line["roofline"] and line["achievable"] is None

@@ -1,7 +1,8 @@
 """The achievable-peak probes (include/ha_probe.h) through the C ABI: the copy
 probe reproduces its source bitwise (ordinary and non-temporal accesses, sizes
-that leave a tail after the four-deep loop), the read, MFMA and issue-overlap
-probes complete, and the binding returns the work each call performs."""
+that leave a tail after the four-deep loop), the read, MFMA (constant and
+random operands) and issue-overlap probes complete, and the binding returns
+the work each call performs."""
 import pytest
 import torch
 
@@ -31,6 +32,8 @@ def test_read_and_mfma_probes_complete():
     assert ha.probe_read(src[:48], sink) == 48
     flops = ha.probe_mfma(8, 16, sink)
     assert flops == 8 * 4 * 4 * 16 * 2 * 32 * 32 * 16
+    assert ha.probe_mfma_data(8, 16, sink) == flops
+    assert ha.probe_mfma_data(8, 17, sink) == 8 * 4 * 4 * 17 * 2 * 32 * 32 * 16   # an odd round count
     torch.cuda.synchronize()
     assert sink.item() == 0.0          # the sinks are written only in cases that cannot occur here
 
