@@ -734,8 +734,11 @@ def run_block(args, w):
     tele = None if args.no_telemetry else sample_telemetry(step, dev)
     peaks = None if args.no_peaks else achievable_peaks(dev)
     if peaks:
+        rnd = peaks.get("mfma_bf16_tflops_random_operands_sustained")
         for k in ("proj_in", "proj_out"):
             gemm[f"{k}_frac_of_achievable"] = round(gemm[f"{k}_tflops"] / peaks["mfma_bf16_tflops"], 4)
+            if rnd:
+                gemm[f"{k}_frac_of_random_operand_mfma"] = round(gemm[f"{k}_tflops"] / rnd, 4)
     print(json.dumps(annotate(line, peaks, tele)), flush=True)
 
 
