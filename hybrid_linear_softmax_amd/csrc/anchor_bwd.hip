@@ -374,32 +374,32 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
   // descriptors of the wave)
   const bool is_a = __builtin_amdgcn_readfirstlane(wave) >= 4;
   // this thread's sub-tile: 4 query rows 4 sm .. 4 sm + 3, features 8 sfg ..
-  // 8 sfg + 7.  Lane l of the tensor's wave w' takes sm = (l & 7) | (l & 16) >> 1
-  // and sfg = 4 w' + (l >> 3 & 1) + (l >> 5 & 1) * 2: any 16 neighbouring lanes
-  // hold 8 sm x 2 sfg, any 32 hold 16 sm x 2 sfg.  The transposed 8-byte writes
-  // (32 lanes at a time) then cover 32 distinct bank pairs; the row-major
-  // 16-byte writes (16 lanes at a time) do too once the threads with sm bit 2
-  // set hold their rows rotated by two, 4 sm + 2, + 3, + 0, + 1, which they
-  // load in that order (so no register moves: a per-lane rotation of the
-  // registers cost 26 vector instructions per step).  Their transposed words
-  // then carry the query pairs swapped; those are the queries with bit 4 set,
-  // the second 16-query half of each 32, and the P and dS operands of that
-  // half are packed with their pairs swapped to match.  (An XOR swizzle of the
-  // rows' 16-byte slots instead measured, with an LDS probe, ~30 % slower for
-  // the tile's fragment reads, four times as frequent as its writes.)
+  // 8 sfg + 7.  LDS writes go 8 lanes (16-byte writes) or 16 lanes (8-byte
+  // writes) at a time with banks repeating every 128 bytes; 16-byte reads see
+  // a wider window (a column swizzle of the transposed tile, conflict-free for
+  // 16-lane groups, made its reads conflict).  Lane l = b0 .. b5 of the
+  // tensor's wave w' takes sm = l mod 16 and sfg = (b1 ^ b4) + 2 (b2 ^ b5) + 4 w':
+  //  * transposed writes: any 16 neighbouring lanes hold 16 distinct sm, i.e.
+  //    16 distinct 8-byte slots of the feature row (the row pitch is a
+  //    multiple of 16 bytes, so sfg does not move the slot);
+  //  * row-major writes: row 4 sm + j, chunk sfg lands on 16-byte slot
+  //    (4 sm + j + sfg) mod 8 (the row pitch is 16 bytes past a multiple of 128),
+  //    and over any 8 neighbouring lanes 4 b0 + (b1 ^ b4) + 2 (b2 ^ b5) takes all
+  //    8 values;
+  //  * a wave still reads 64 contiguous bytes of each of 16 rows per load.
+  // Both kinds of commit write are then conflict-free, and the tiles keep the
+  // layout their readers expect.  (The previous map, 8 sm x 2 sfg per 16 lanes
+  // with half the threads' rows rotated, had both kinds collide two ways: half
+  // of the commit's LDS cycles were bank conflicts.)
   const int ll = sub & 63;
-  const int sfg = 4 * (sub >> 6) + ((ll >> 3) & 1) + 2 * ((ll >> 5) & 1);
-  const int sm = (ll & 7) | ((ll & 16) >> 1);
-  const int rot = 2 * ((sm >> 2) & 1);
+  const int sm = ll & 15;
+  const int sfg = (((ll >> 1) ^ (ll >> 4)) & 1) | ((((ll >> 2) ^ (ll >> 5)) & 1) << 1) | (4 * (sub >> 6));
   const __amdgpu_buffer_rsrc_t rsrc = is_a ? rA : rQ;
   bf16_t* dst_row = is_a ? sA : sQ;
   bf16_t* dst_t = is_a ? sAt : sQt;
-  // rows 4 sm + rot, + 1 and 4 sm + (rot ^ 2), + 1: two lane offsets, the step
-  // in the scalar offset
-  const int offA = (4 * sm + rot) * (D * 2) + sfg * 16;
-  const int offB = (4 * sm + (rot ^ 2)) * (D * 2) + sfg * 16;
-  bf16_t* rowA = dst_row + (4 * sm + rot) * KP + 8 * sfg;
-  bf16_t* rowB = dst_row + (4 * sm + (rot ^ 2)) * KP + 8 * sfg;
+  // rows 4 sm .. 4 sm + 3: one lane offset, the step in the scalar offset
+  const int offA = 4 * sm * (D * 2) + sfg * 16;
+  bf16_t* rowA = dst_row + 4 * sm * KP + 8 * sfg;
   uint4 pre[4];
   // lse and D of the next step's queries, as loaded: they are first used at the
   // commit, so the loads stay in flight during the step's MFMAs (scaling lse
@@ -414,10 +414,9 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
   auto fetch = [&](int64_t q0) {
     if (loader) {
       const int soff = static_cast<int>(q0 * (D * 2));
-      pre[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offA, soff, 0));
-      pre[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offA + D * 2, soff, 0));
-      pre[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offB, soff, 0));
-      pre[3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offB + D * 2, soff, 0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pre[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, offA + j * (D * 2), soff, 0));
     }
     if (tid < BQ) {
       preQ = static_cast<int>(q0) + tid;
@@ -439,10 +438,8 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
         *reinterpret_cast<uint2*>(&dst_t[(8 * sfg + 2 * p + 1) * TP + pos]) =
             make_uint2(__builtin_amdgcn_perm(r1[p], r0[p], 0x07060302u), __builtin_amdgcn_perm(r3[p], r2[p], 0x07060302u));
       }
-      *reinterpret_cast<uint4*>(rowA) = pre[0];
-      *reinterpret_cast<uint4*>(rowA + KP) = pre[1];
-      *reinterpret_cast<uint4*>(rowB) = pre[2];
-      *reinterpret_cast<uint4*>(rowB + KP) = pre[3];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(rowA + j * KP) = pre[j];
     }
     if (tid < BQ) {
       // a query past N contributes nothing: P = exp2(s c - inf) = 0
@@ -451,6 +448,8 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
     }
   };
 
+  // column of this lane's transposed-tile fragments: queries 32 th + 8 h
+  const int tcol = 32 * th + 8 * h;
   const int64_t nqb = (N + BQ - 1) / BQ;
   fetch(0);
   for (int64_t qb = 0; qb < nqb; ++qb) {
@@ -507,15 +506,11 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
       pk.z = pack_bf16(p[8 * tt + 4], p[8 * tt + 5]); pk.w = pack_bf16(p[8 * tt + 6], p[8 * tt + 7]);
       dk4.x = pack_bf16(ds[8 * tt + 0], ds[8 * tt + 1]); dk4.y = pack_bf16(ds[8 * tt + 2], ds[8 * tt + 3]);
       dk4.z = pack_bf16(ds[8 * tt + 4], ds[8 * tt + 5]); dk4.w = pack_bf16(ds[8 * tt + 6], ds[8 * tt + 7]);
-      if (tt == 1) {   // the transposed tiles hold these queries' pairs swapped
-        pk = make_uint4(pk.y, pk.x, pk.w, pk.z);
-        dk4 = make_uint4(dk4.y, dk4.x, dk4.w, dk4.z);
-      }
       const bf16x8 pf = as_bf16x8(pk), dsf = as_bf16x8(dk4);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const bf16x8 at = *reinterpret_cast<const bf16x8*>(&sAt[(32 * rb + l32) * TP + 32 * t + 16 * tt + 8 * h]);
-        const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&sQt[(32 * rb + l32) * TP + 32 * t + 16 * tt + 8 * h]);
+        const bf16x8 at = *reinterpret_cast<const bf16x8*>(&sAt[(32 * rb + l32) * TP + tcol + 16 * tt]);
+        const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&sQt[(32 * rb + l32) * TP + tcol + 16 * tt]);
         dv[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pf, dv[rb], 0, 0, 0);
         dk[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf, dk[rb], 0, 0, 0);
         if (tt == 0 && rb < 2) {
