@@ -364,8 +364,7 @@ __global__ __launch_bounds__(512, 1) void sm_bwd_dkv_bf16(const bf16_t* __restri
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[rb][r] = 0.f; dv[rb][r] = 0.f; }
 
-  // this thread's sub-tile of the next query step: tensor (Q or da), 4 query
-  // rows 4 m .. 4 m + 3, features 8 fg .. 8 fg + 7
+  // each thread stages a sub-tile of the next query step's Q or da rows
   const int sub = tid & 255;
   const bool loader = sub < TSUB;
   // waves 0-3 fetch Q, waves 4-7 da: the choice is taken from a wave-uniform
