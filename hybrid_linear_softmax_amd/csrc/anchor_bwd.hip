@@ -195,7 +195,12 @@ __global__ __launch_bounds__(512) void sm_bwd_dq_bf16(const bf16_t* __restrict__
     constexpr bool MASKED = decltype(masked)::value;
     const int64_t k0 = kb * BK;
     if (tid < TSUB) {   // K^T: 4 keys x 8 features per thread
-      const int fg = tid / (BK / 4), m = tid % (BK / 4);
+      // keys 4 m .. 4 m + 3 with m = tid mod 16 (16 distinct m per 16 lanes: the
+      // transposed 8-byte writes hit distinct slots); the feature group is
+      // XOR-ed with lane bits 1-2 so that 8 neighbouring lanes, which share the
+      // chunk swizzle of rows 4 m + j two by two, read distinct 16-byte slots
+      const int m = tid % (BK / 4);
+      const int fg = (tid / (BK / 4)) ^ (((tid >> 1) & 1) | (((tid >> 2) & 1) << 1));
       uint4 r[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
